@@ -1,0 +1,184 @@
+/*
+ * pka.h -- prefix-KV chunk attention for context-frozen training (MI355X, gfx950).
+ *
+ * The method (pages cited by title and section):
+ *  - "Context-Frozen Training", The Solution: a no-grad forward of the context builds
+ *    its KV cache (Phase 1); the decision tokens then run forward and backward against
+ *    that frozen cache (Phase 2); gradients flow through the decision tokens only.
+ *  - "train: walk the window" (llama.cpp), What it is / Contents: each reply chunk is
+ *    trained against the cached prefix, which it reads as constants stored at F16 or
+ *    q8_0; the chunk is then re-decoded into the cache so the next chunk sees it.
+ *    Approval comment: V is cached untransposed (so it can be quantised) and the cache
+ *    type should follow the serving context, i.e. it is a call argument here.
+ *  - "stop-gradient through context tokens" (prime-rl), Known gaps: an attention
+ *    backward that produces gradient for the kept (chunk) queries only.
+ *
+ * Shapes: B windows, Hq query heads, Hkv KV heads (G = Hq/Hkv query heads share KV
+ * head h/G), head_dim D, prefix (cached context) length P, chunk length C. Chunk
+ * query i (token P+i of the window) attends to prefix keys 0..P-1 and chunk keys
+ * 0..i (causal attention offset by P). The prefix gets no gradient: it is a constant.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates nothing and keeps no state between calls (except the opt-in
+ *    profiling counters at the end of this file).
+ *  - Layouts are dense row-major with the innermost dimension contiguous:
+ *      q, o, dO, dq        bf16 [B][Hq][C][D]
+ *      k, v, dk, dv        bf16 [B][Hkv][C][D]     (the chunk's own keys/values)
+ *      lse, delta          f32  [B][Hq][C]
+ *      cache k, v          F16/BF16: u16 [B][Hkv][capacity][D]
+ *                          Q8_0:     int8 [B][Hkv][capacity][D]
+ *      cache k/v scales    Q8_0 only: f16 [B][Hkv][capacity][D/32]
+ *    Every base pointer must be 16-byte aligned.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null stream)
+ *    and never synchronises the host.
+ *  - Arguments are validated on the host before any HIP call; on failure nothing is
+ *    launched and a non-zero pka_status is returned (never an abort or exception),
+ *    mirroring the walk's failure exit in "train: walk the window" (rebase comment:
+ *    a failed chunk step returns false, like a refused graph). A launch failure
+ *    returns PKA_ERR_HIP. pka_last_error() gives a message for the calling thread.
+ *  - Calls that overlap on one stream are ordered; calls on different streams that
+ *    share output buffers race (the caller orders them).
+ *  - Limits: D in {64, 128}; 1 <= C <= 65536; 0 <= P; P + C <= 2^31 - 1;
+ *    B * Hq * C <= 2^31 - 1.
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* pka_stream_t; /* identical to hipStream_t */
+
+typedef enum {
+  PKA_OK = 0,
+  PKA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+  PKA_ERR_DIMS = 2,        /* inconsistent or out-of-range dimensions           */
+  PKA_ERR_UNSUPPORTED = 3, /* head_dim or cache type this library does not serve */
+  PKA_ERR_CAPACITY = 4,    /* the cache is too short for the rows addressed     */
+  PKA_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                  */
+  PKA_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required        */
+  PKA_ERR_HIP = 7          /* a HIP launch failed                               */
+} pka_status;
+
+typedef enum {
+  PKA_CACHE_F16 = 0,  /* IEEE half; read as bf16 (round to nearest even)          */
+  PKA_CACHE_BF16 = 1, /* bf16, read as is                                         */
+  PKA_CACHE_Q8_0 = 2  /* blocks of 32 int8 codes along D + one fp16 scale per block:
+                         value = f32(scale) * code, read as bf16 (RNE)            */
+} pka_cache_type;
+
+/* One chunk step, uniform over the B windows. */
+typedef struct {
+  int32_t batch;       /* B >= 1                                    */
+  int32_t n_heads_q;   /* Hq >= 1, a multiple of n_heads_kv         */
+  int32_t n_heads_kv;  /* Hkv >= 1                                  */
+  int32_t head_dim;    /* D: 64 or 128                              */
+  int64_t prefix_len;  /* P >= 0: cached context rows 0..P-1 are read */
+  int64_t chunk_len;   /* C >= 1                                    */
+  float softmax_scale; /* > 0 and finite; usually 1/sqrt(D)         */
+} pka_dims;
+
+/* The frozen prefix cache of B windows x Hkv heads x capacity token rows. */
+typedef struct {
+  int32_t type;      /* pka_cache_type                                         */
+  int32_t head_dim;  /* must equal pka_dims.head_dim                           */
+  int64_t capacity;  /* rows per (window, KV head)                             */
+  void* k;           /* F16/BF16: u16[B][Hkv][cap][D]; Q8_0: int8[B][Hkv][cap][D] */
+  void* v;
+  void* k_scale;     /* Q8_0: f16[B][Hkv][cap][D/32]; NULL for F16/BF16          */
+  void* v_scale;
+} pka_cache;
+
+/* Workspace (bytes) the calls below need for this shape; 0 means none. The amount
+ * depends only on the dims (the split of the prefix over workgroups is planned for
+ * the 256 compute units of an MI355X). */
+size_t pka_fwd_workspace_bytes(const pka_dims* dims);
+size_t pka_bwd_workspace_bytes(const pka_dims* dims);
+
+/* Forward of chunk attention against the frozen prefix ("Context-Frozen Training",
+ * The Solution, Phase 2; "train: walk the window", What it is).
+ *   o[b][h][i]   = sum_j softmax_j(scale * q[b][h][i] . K_j) V_j over allowed j
+ *   lse[b][h][i] = ln sum_j exp(scale * q[b][h][i] . K_j) over allowed j (natural log)
+ * where K_j, V_j (j < P) are cache rows of KV head h/G and K_{P+t}, V_{P+t} = k, v
+ * rows t of the chunk; row i allows j <= P + i. Reads cache rows [0, P) only.
+ * ws: pka_fwd_workspace_bytes(dims) bytes of device memory (may be NULL if 0). */
+pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k,
+                              const void* v, const pka_cache* cache, void* o,
+                              float* lse, void* ws, size_t ws_bytes,
+                              pka_stream_t stream);
+
+/* Backward of the forward above from the upstream gradient d_o on the chunk rows.
+ * Computes delta = rowsum(d_o * o), then
+ *   dq = scale * dS K      over prefix and chunk keys,
+ *   dk = scale * dS^T q,  dv = P^T d_o   for the chunk's own C keys only,
+ * with P = exp(scale q K^T - lse) (masked) and dS = P * (d_o V^T - delta); dk, dv
+ * are summed over the G query heads of each KV head. The prefix gets no gradient:
+ * its rows are stop-gradient constants ("train: walk the window", Why it's a draft;
+ * "stop-gradient through context tokens", Known gaps: grad for kept queries only).
+ * o and lse are the forward's outputs. delta (f32 [B][Hq][C]) is written if not
+ * NULL. ws: pka_bwd_workspace_bytes(dims) bytes (always > 0). */
+pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k,
+                              const void* v, const pka_cache* cache, const void* o,
+                              const float* lse, const void* d_o, void* dq, void* dk,
+                              void* dv, float* delta, void* ws, size_t ws_bytes,
+                              pka_stream_t stream);
+
+/* Re-decode of the chunk into the cache ("train: walk the window", What it is and
+ * Contents): writes cache rows [P, P+C) of every (window, KV head) from k, v
+ * (bf16 [B][Hkv][C][D]). Uses batch, n_heads_kv, head_dim, prefix_len, chunk_len of
+ * dims; requires P + C <= capacity and a cache of the matching type.
+ *  q8_0: per block of 32 values along D: amax = max|x|, d = amax/127 (IEEE fp32
+ *        division), scale = fp16(d) (RNE), code = clamp(round_half_away(x/d), +-127)
+ *        with the fp32 d; an all-zero block stores scale 0 and codes 0.
+ *  f16:  fp16(x) with round to nearest even.      bf16: a copy. */
+pka_status pka_kv_append_q8_0(const pka_dims* dims, const void* k, const void* v,
+                              const pka_cache* cache, pka_stream_t stream);
+pka_status pka_kv_append_f16(const pka_dims* dims, const void* k, const void* v,
+                             const pka_cache* cache, pka_stream_t stream);
+pka_status pka_kv_append_bf16(const pka_dims* dims, const void* k, const void* v,
+                              const pka_cache* cache, pka_stream_t stream);
+
+/* Test hook: dequantise rows [row0, row0+rows) of both K and V of a Q8_0 cache of
+ * `batch` windows x `n_heads_kv` heads exactly as the attention kernels read them:
+ * out_f32 = f32(scale) * code (exact), out_bf16 = bf16(out_f32) (RNE, may be NULL).
+ * Outputs are [2][batch][n_heads_kv][rows][D] (K first, then V). */
+pka_status pka_kv_dequant_q8_0(const pka_cache* cache, int32_t batch,
+                               int32_t n_heads_kv, int64_t row0, int64_t rows,
+                               float* out_f32, void* out_bf16, pka_stream_t stream);
+
+/* A static description of a status code. */
+const char* pka_status_string(pka_status status);
+/* The message of the last failed call on this thread ("" if none). */
+const char* pka_last_error(void);
+
+/* Opt-in kernel timing for benchmarks. When enabled, each kernel launch is
+ * bracketed by two HIP events recorded on the call's stream; pka_profile_read
+ * synchronises on those events and returns the summed elapsed milliseconds and
+ * the number of launches of one kernel since the last reset. At most 65536 launches
+ * per kernel are recorded between resets (later ones are counted in `dropped`). */
+typedef enum {
+  PKA_KERNEL_FWD = 0,        /* forward tiles (one launch per pka_chunk_attn_fwd) */
+  PKA_KERNEL_FWD_COMBINE = 1,/* merge of prefix splits                            */
+  PKA_KERNEL_BWD_PREP = 2,   /* delta = rowsum(dO * O)                             */
+  PKA_KERNEL_BWD_DQ = 3,     /* dq over prefix and chunk keys                      */
+  PKA_KERNEL_BWD_DKDV = 4,   /* chunk-only dk, dv                                  */
+  PKA_KERNEL_BWD_DQ_REDUCE = 5, /* sum of dq split partials                        */
+  PKA_KERNEL_APPEND = 6,     /* kv_append_*                                        */
+  PKA_KERNEL_DEQUANT = 7,    /* kv_dequant_q8_0                                    */
+  PKA_KERNEL_COUNT = 8
+} pka_kernel_id;
+
+pka_status pka_profile_enable(int32_t on);
+pka_status pka_profile_reset(void);
+pka_status pka_profile_read(int32_t kernel, double* total_ms, int64_t* launches,
+                            int64_t* dropped);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PKA_H */

@@ -1,0 +1,275 @@
+"""Python binding of libpka (prefix-KV chunk attention on MI355X).
+
+Argument marshalling only: every computation runs in the HIP kernels of
+``libpka.so`` (built by ``python prefix_kv_attention_amd/build.py``). PyTorch
+provides device memory and the current HIP stream. Importing this package raises
+if the library is missing; there is no fallback implementation.
+
+Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
+``chunk_attn_fwd``, ``chunk_attn_bwd``, ``kv_append_q8_0``, ``kv_append_f16``,
+``kv_append_bf16``, ``kv_dequant_q8_0``, ``fwd_workspace_bytes``,
+``bwd_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
+autograd function whose cache inputs get no gradient (they are stop-gradient
+constants: "train: walk the window", Why it's a draft).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpka.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python prefix_kv_attention_amd/build.py`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+CACHE_F16, CACHE_BF16, CACHE_Q8_0 = 0, 1, 2
+CACHE_TYPE_BY_NAME = {"f16": CACHE_F16, "bf16": CACHE_BF16, "q8_0": CACHE_Q8_0}
+STATUS = {0: "PKA_OK", 1: "PKA_ERR_NULL", 2: "PKA_ERR_DIMS", 3: "PKA_ERR_UNSUPPORTED",
+          4: "PKA_ERR_CAPACITY", 5: "PKA_ERR_ALIGN", 6: "PKA_ERR_WORKSPACE", 7: "PKA_ERR_HIP"}
+KERNELS = {"fwd": 0, "fwd_combine": 1, "bwd_prep": 2, "bwd_dq": 3, "bwd_dkdv": 4,
+           "bwd_dq_reduce": 5, "append": 6, "dequant": 7}
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
+                ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("prefix_len", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+_P = ctypes.POINTER
+_vp, _sz, _i32, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+_SIGS = {
+    "pka_fwd_workspace_bytes": (_sz, [_P(Dims)]),
+    "pka_bwd_workspace_bytes": (_sz, [_P(Dims)]),
+    "pka_chunk_attn_fwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
+                                          _vp, _sz, _vp]),
+    "pka_chunk_attn_bwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
+                                          _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pka_kv_append_q8_0": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
+    "pka_kv_append_f16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
+    "pka_kv_append_bf16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
+    "pka_kv_dequant_q8_0": (ctypes.c_int, [_P(CacheDesc), _i32, _i32, _i64, _i64, _vp, _vp,
+                                           _vp]),
+    "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pka_last_error": (ctypes.c_char_p, []),
+    "pka_profile_enable": (ctypes.c_int, [_i32]),
+    "pka_profile_reset": (ctypes.c_int, []),
+    "pka_profile_read": (ctypes.c_int, [_i32, _P(ctypes.c_double), _P(_i64), _P(_i64)]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+lib = _lib
+
+
+class PkaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.pka_last_error().decode() or _lib.pka_status_string(status).decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PkaError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_dims(batch, n_heads_q, n_heads_kv, head_dim, prefix_len, chunk_len,
+              softmax_scale) -> Dims:
+    return Dims(int(batch), int(n_heads_q), int(n_heads_kv), int(head_dim),
+                int(prefix_len), int(chunk_len), float(softmax_scale))
+
+
+class PrefixCache:
+    """Device tensors of a prefix cache [B][Hkv][capacity][D] in one storage type."""
+
+    def __init__(self, cache_type: str, k, v, k_scale=None, v_scale=None):
+        if cache_type not in CACHE_TYPE_BY_NAME:
+            raise ValueError(f"unknown cache type {cache_type!r}")
+        self.cache_type = cache_type
+        self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
+        self.batch, self.n_heads_kv, self.capacity, self.head_dim = k.shape
+
+    @classmethod
+    def empty(cls, cache_type, batch, n_heads_kv, capacity, head_dim, device="cuda"):
+        shape = (batch, n_heads_kv, capacity, head_dim)
+        if cache_type == "q8_0":
+            sshape = (batch, n_heads_kv, capacity, head_dim // 32)
+            return cls(cache_type,
+                       torch.empty(shape, dtype=torch.int8, device=device),
+                       torch.empty(shape, dtype=torch.int8, device=device),
+                       torch.empty(sshape, dtype=torch.float16, device=device),
+                       torch.empty(sshape, dtype=torch.float16, device=device))
+        dt = torch.float16 if cache_type == "f16" else torch.bfloat16
+        return cls(cache_type, torch.empty(shape, dtype=dt, device=device),
+                   torch.empty(shape, dtype=dt, device=device))
+
+    def desc(self) -> CacheDesc:
+        return CacheDesc(CACHE_TYPE_BY_NAME[self.cache_type], int(self.head_dim),
+                         int(self.capacity), self.k.data_ptr(), self.v.data_ptr(),
+                         self.k_scale.data_ptr() if self.k_scale is not None else None,
+                         self.v_scale.data_ptr() if self.v_scale is not None else None)
+
+
+def _chunk_dims(q, k, prefix_len, scale):
+    B, Hq, C, D = q.shape
+    Hkv = k.shape[1]
+    return make_dims(B, Hq, Hkv, D, prefix_len, C, scale)
+
+
+def _need(t, name, dtype=torch.bfloat16):
+    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def fwd_workspace_bytes(dims: Dims) -> int:
+    return int(_lib.pka_fwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def bwd_workspace_bytes(dims: Dims) -> int:
+    return int(_lib.pka_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
+                   o=None, lse=None, ws=None):
+    """O [B][Hq][C][D] bf16 and LSE [B][Hq][C] f32 of the chunk against the prefix."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    dims = _chunk_dims(q, k, prefix_len, scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(fwd_workspace_bytes(dims), q.device)
+    cd = cache.desc()
+    _check(_lib.pka_chunk_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                   ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(q.device)),
+           "pka_chunk_attn_fwd")
+    return o, lse
+
+
+def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o, lse,
+                   d_o, dq=None, dk=None, dv=None, delta=None, ws=None):
+    """dQ (chunk rows), dK and dV (the chunk's own keys); the prefix gets nothing."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
+        _need(t, n)
+    _need(lse, "lse", torch.float32)
+    dims = _chunk_dims(q, k, prefix_len, scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if ws is None:
+        ws = _workspace(bwd_workspace_bytes(dims), q.device)
+    cd = cache.desc()
+    _check(_lib.pka_chunk_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                   ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(d_o),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(q.device)),
+           "pka_chunk_attn_bwd")
+    return dq, dk, dv
+
+
+def _append(fn, name, k, v, cache: PrefixCache, prefix_len: int):
+    _need(k, "k")
+    _need(v, "v")
+    B, Hkv, C, D = k.shape
+    dims = make_dims(B, Hkv, Hkv, D, prefix_len, C, 1.0)
+    cd = cache.desc()
+    _check(fn(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(cd), _stream(k.device)), name)
+
+
+def kv_append_q8_0(k, v, cache: PrefixCache, prefix_len: int):
+    """Quantise the chunk's K/V (bf16 [B][Hkv][C][D]) into cache rows [P, P+C)."""
+    _append(_lib.pka_kv_append_q8_0, "pka_kv_append_q8_0", k, v, cache, prefix_len)
+
+
+def kv_append_f16(k, v, cache: PrefixCache, prefix_len: int):
+    _append(_lib.pka_kv_append_f16, "pka_kv_append_f16", k, v, cache, prefix_len)
+
+
+def kv_append_bf16(k, v, cache: PrefixCache, prefix_len: int):
+    _append(_lib.pka_kv_append_bf16, "pka_kv_append_bf16", k, v, cache, prefix_len)
+
+
+def kv_append(k, v, cache: PrefixCache, prefix_len: int):
+    """Append in the cache's own storage type."""
+    {"q8_0": kv_append_q8_0, "f16": kv_append_f16, "bf16": kv_append_bf16}[
+        cache.cache_type](k, v, cache, prefix_len)
+
+
+def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = True):
+    """(f32, bf16 or None) [2][B][Hkv][rows][D]: cache rows as the attention reads them."""
+    shape = (2, cache.batch, cache.n_heads_kv, rows, cache.head_dim)
+    out = torch.empty(shape, dtype=torch.float32, device=cache.k.device)
+    outb = torch.empty(shape, dtype=torch.bfloat16, device=cache.k.device) if want_bf16 else None
+    cd = cache.desc()
+    _check(_lib.pka_kv_dequant_q8_0(ctypes.byref(cd), cache.batch, cache.n_heads_kv, row0, rows,
+                                    _ptr(out), _ptr(outb), _stream(cache.k.device)),
+           "pka_kv_dequant_q8_0")
+    return out, outb
+
+
+class _ChunkAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, cache, prefix_len, scale):
+        o, lse = chunk_attn_fwd(q, k, v, cache, prefix_len, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.cache, ctx.prefix_len, ctx.scale = cache, prefix_len, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = chunk_attn_bwd(q, k, v, ctx.cache, ctx.prefix_len, ctx.scale, o, lse,
+                                    d_o.contiguous())
+        return dq, dk, dv, None, None, None
+
+
+def chunk_attention(q, k, v, cache: PrefixCache, prefix_len: int, scale: float):
+    """Autograd op: O of the chunk; gradients reach q, k, v only (never the cache)."""
+    return _ChunkAttention.apply(q, k, v, cache, prefix_len, scale)
+
+
+def profile_enable(on: bool = True):
+    _check(_lib.pka_profile_enable(1 if on else 0), "pka_profile_enable")
+
+
+def profile_reset():
+    _check(_lib.pka_profile_reset(), "pka_profile_reset")
+
+
+def profile_read(kernel: str):
+    """(total_ms, launches, dropped) of one kernel since the last reset."""
+    ms, n, dr = ctypes.c_double(), ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.pka_profile_read(KERNELS[kernel], ctypes.byref(ms), ctypes.byref(n),
+                                 ctypes.byref(dr)), "pka_profile_read")
+    return ms.value, n.value, dr.value

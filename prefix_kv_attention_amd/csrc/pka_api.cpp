@@ -1,0 +1,423 @@
+// C-ABI host layer of libpka: argument validation (before any HIP call), work
+// planning, workspace layout and kernel launches. See include/pka.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "pka_internal.hpp"
+
+namespace pka {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pka_status fail(pka_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pka_status hip_fail(hipError_t e, const char* what) {
+  return fail(PKA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+constexpr int64_t kMaxChunk = 65536;
+constexpr int64_t kMaxSeq = 2147483647LL;
+
+pka_status check_dims(const pka_dims* d) {
+  if (!d) return fail(PKA_ERR_NULL, "dims is NULL");
+  if (d->batch < 1 || d->n_heads_q < 1 || d->n_heads_kv < 1)
+    return fail(PKA_ERR_DIMS, "batch, n_heads_q and n_heads_kv must be >= 1");
+  if (d->n_heads_q % d->n_heads_kv != 0)
+    return fail(PKA_ERR_DIMS, "n_heads_q (%d) is not a multiple of n_heads_kv (%d)",
+                d->n_heads_q, d->n_heads_kv);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(PKA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->prefix_len < 0) return fail(PKA_ERR_DIMS, "prefix_len < 0");
+  if (d->chunk_len < 1 || d->chunk_len > kMaxChunk)
+    return fail(PKA_ERR_DIMS, "chunk_len must be in [1, %lld]", (long long)kMaxChunk);
+  if (d->prefix_len > kMaxSeq - d->chunk_len)
+    return fail(PKA_ERR_DIMS, "prefix_len + chunk_len exceeds 2^31 - 1");
+  const int64_t nrow = (int64_t)d->batch * d->n_heads_q * d->chunk_len;
+  if (nrow > kMaxSeq) return fail(PKA_ERR_DIMS, "batch * n_heads_q * chunk_len exceeds 2^31 - 1");
+  if ((int64_t)(d->n_heads_q / d->n_heads_kv) * d->chunk_len > kMaxSeq)
+    return fail(PKA_ERR_DIMS, "group * chunk_len exceeds 2^31 - 1");
+  if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
+    return fail(PKA_ERR_DIMS, "softmax_scale must be finite and > 0");
+  return PKA_OK;
+}
+
+// rows_needed: cache rows the call addresses (P for attention, P + C for appends).
+pka_status check_cache(const pka_cache* c, const pka_dims* d, int64_t rows_needed,
+                       bool writes) {
+  if (!c) return fail(PKA_ERR_NULL, "cache is NULL");
+  if (c->type != PKA_CACHE_F16 && c->type != PKA_CACHE_BF16 && c->type != PKA_CACHE_Q8_0)
+    return fail(PKA_ERR_UNSUPPORTED, "unknown cache type %d", c->type);
+  if (c->head_dim != d->head_dim)
+    return fail(PKA_ERR_DIMS, "cache head_dim %d != dims head_dim %d", c->head_dim, d->head_dim);
+  if (c->capacity < 0) return fail(PKA_ERR_DIMS, "cache capacity < 0");
+  if (rows_needed > c->capacity)
+    return fail(PKA_ERR_CAPACITY, "cache capacity %lld < %lld rows addressed",
+                (long long)c->capacity, (long long)rows_needed);
+  if (rows_needed > 0 || writes) {
+    if (!c->k || !c->v) return fail(PKA_ERR_NULL, "cache k/v is NULL");
+    if (!aligned16(c->k) || !aligned16(c->v))
+      return fail(PKA_ERR_ALIGN, "cache k/v not 16-byte aligned");
+    if (c->type == PKA_CACHE_Q8_0) {
+      if (!c->k_scale || !c->v_scale) return fail(PKA_ERR_NULL, "q8_0 cache scales are NULL");
+      if (!aligned16(c->k_scale) || !aligned16(c->v_scale))
+        return fail(PKA_ERR_ALIGN, "q8_0 cache scales not 16-byte aligned");
+    }
+  }
+  return PKA_OK;
+}
+
+pka_status check_ptrs(std::initializer_list<const void*> ptrs, const char* names) {
+  for (const void* ptr : ptrs) {
+    if (!ptr) return fail(PKA_ERR_NULL, "a required tensor pointer is NULL (%s)", names);
+    if (!aligned16(ptr)) return fail(PKA_ERR_ALIGN, "a tensor pointer is not 16-byte aligned (%s)", names);
+  }
+  return PKA_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+CacheRef cache_ref(const pka_cache* c) {
+  CacheRef r;
+  r.k = c->k;
+  r.v = c->v;
+  r.ks = static_cast<const uint16_t*>(c->k_scale);
+  r.vs = static_cast<const uint16_t*>(c->v_scale);
+  r.cap = c->capacity;
+  return r;
+}
+
+// ---------------------------------------------------------------- profiling
+constexpr int kMaxRecords = 65536;
+struct ProfSlot {
+  std::vector<hipEvent_t> begin, end;  // pooled events, reused across resets
+  int64_t used = 0;
+  int64_t dropped = 0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+ProfSlot g_prof[PKA_KERNEL_COUNT];
+
+}  // namespace
+
+void prof_begin(int kernel, hipStream_t s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfSlot& sl = g_prof[kernel];
+  if (sl.used >= kMaxRecords) {
+    ++sl.dropped;
+    return;
+  }
+  if ((int64_t)sl.begin.size() <= sl.used) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
+    }
+    sl.begin.push_back(a);
+    sl.end.push_back(b);
+  }
+  (void)hipEventRecord(sl.begin[sl.used], s);
+}
+
+void prof_end(int kernel, hipStream_t s) {
+  if (!g_prof_on) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfSlot& sl = g_prof[kernel];
+  if (sl.used >= kMaxRecords || (int64_t)sl.end.size() <= sl.used) return;
+  (void)hipEventRecord(sl.end[sl.used], s);
+  ++sl.used;
+}
+
+// One row block is 128 packed rows of one (window, KV head). When these units
+// cannot give every CU two workgroups, the key tiles are split; each split keeps
+// at least 8 tiles so the merge stays small next to the work.
+static Plan make_plan(const pka_dims& d) {
+  Plan pl;
+  const int64_t G = d.n_heads_q / d.n_heads_kv;
+  pl.n_rb = (int)((G * d.chunk_len + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t units = (int64_t)d.batch * d.n_heads_kv * pl.n_rb;
+  const int64_t target = 2 * kNumCUs;
+  int split = 1;
+  if (units < target) {
+    split = (int)((target + units - 1) / units);
+    const int64_t min_tiles = (d.prefix_len + 1 + kKeysPerTile - 1) / kKeysPerTile;
+    const int64_t max_split = min_tiles / 8 > 1 ? min_tiles / 8 : 1;
+    if (split > max_split) split = (int)max_split;
+    if (split > 16) split = 16;
+  }
+  pl.n_split = split;
+  pl.nblk = (int)(units * split);
+  return pl;
+}
+
+Plan plan_fwd(const pka_dims& d) { return make_plan(d); }
+Plan plan_bwd(const pka_dims& d) { return make_plan(d); }
+
+}  // namespace pka
+
+using namespace pka;
+
+extern "C" {
+
+const char* pka_status_string(pka_status st) {
+  switch (st) {
+    case PKA_OK: return "ok";
+    case PKA_ERR_NULL: return "a required pointer is NULL";
+    case PKA_ERR_DIMS: return "inconsistent or out-of-range dimensions";
+    case PKA_ERR_UNSUPPORTED: return "unsupported head_dim or cache type";
+    case PKA_ERR_CAPACITY: return "cache capacity too small";
+    case PKA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case PKA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* pka_last_error(void) { return g_last_error; }
+
+size_t pka_fwd_workspace_bytes(const pka_dims* dims) {
+  if (check_dims(dims) != PKA_OK) return 0;
+  const Plan pl = plan_fwd(*dims);
+  if (pl.n_split == 1) return 0;
+  const size_t nrow = (size_t)dims->batch * dims->n_heads_q * dims->chunk_len;
+  return align256((size_t)pl.n_split * nrow * dims->head_dim * 4) +
+         align256((size_t)pl.n_split * nrow * 4);
+}
+
+size_t pka_bwd_workspace_bytes(const pka_dims* dims) {
+  if (check_dims(dims) != PKA_OK) return 0;
+  const Plan pl = plan_bwd(*dims);
+  const size_t nrow = (size_t)dims->batch * dims->n_heads_q * dims->chunk_len;
+  size_t bytes = align256(nrow * 4);  // delta
+  if (pl.n_split > 1) bytes += align256((size_t)pl.n_split * nrow * dims->head_dim * 4);
+  return bytes;
+}
+
+pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k,
+                              const void* v, const pka_cache* cache, void* o, float* lse,
+                              void* ws, size_t ws_bytes, pka_stream_t stream) {
+  g_last_error[0] = 0;
+  pka_status st;
+  if ((st = check_dims(dims)) != PKA_OK) return st;
+  if ((st = check_ptrs({q, k, v, o, lse}, "q, k, v, o, lse")) != PKA_OK) return st;
+  if ((st = check_cache(cache, dims, dims->prefix_len, false)) != PKA_OK) return st;
+  const size_t need = pka_fwd_workspace_bytes(dims);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(PKA_ERR_WORKSPACE, "forward needs %zu workspace bytes, got %zu", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(PKA_ERR_ALIGN, "workspace not 16-byte aligned");
+  }
+  FwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = static_cast<const uint16_t*>(k);
+  p.vc = static_cast<const uint16_t*>(v);
+  p.cache = cache_ref(cache);
+  p.o = static_cast<uint16_t*>(o);
+  p.lse = lse;
+  p.B = dims->batch;
+  p.Hq = dims->n_heads_q;
+  p.Hkv = dims->n_heads_kv;
+  p.G = dims->n_heads_q / dims->n_heads_kv;
+  p.P = dims->prefix_len;
+  p.C = dims->chunk_len;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = (float)((double)dims->softmax_scale * 1.4426950408889634);
+  p.plan = plan_fwd(*dims);
+  if (p.plan.n_split > 1) {
+    const size_t nrow = (size_t)p.B * p.Hq * p.C;
+    p.ws_o = static_cast<float*>(ws);
+    p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                        align256((size_t)p.plan.n_split * nrow * dims->head_dim * 4));
+  }
+  hipError_t e = launch_fwd(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk_attn_fwd launch");
+  return PKA_OK;
+}
+
+pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k,
+                              const void* v, const pka_cache* cache, const void* o,
+                              const float* lse, const void* d_o, void* dq, void* dk, void* dv,
+                              float* delta, void* ws, size_t ws_bytes, pka_stream_t stream) {
+  g_last_error[0] = 0;
+  pka_status st;
+  if ((st = check_dims(dims)) != PKA_OK) return st;
+  if ((st = check_ptrs({q, k, v, o, lse, d_o, dq, dk, dv}, "q, k, v, o, lse, d_o, dq, dk, dv")) !=
+      PKA_OK)
+    return st;
+  if (delta && !aligned16(delta)) return fail(PKA_ERR_ALIGN, "delta not 16-byte aligned");
+  if ((st = check_cache(cache, dims, dims->prefix_len, false)) != PKA_OK) return st;
+  const size_t need = pka_bwd_workspace_bytes(dims);
+  if (!ws || ws_bytes < need)
+    return fail(PKA_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", need,
+                ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(PKA_ERR_ALIGN, "workspace not 16-byte aligned");
+  BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.kc = static_cast<const uint16_t*>(k);
+  p.vc = static_cast<const uint16_t*>(v);
+  p.cache = cache_ref(cache);
+  p.o = static_cast<const uint16_t*>(o);
+  p.lse = lse;
+  p.d_o = static_cast<const uint16_t*>(d_o);
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.B = dims->batch;
+  p.Hq = dims->n_heads_q;
+  p.Hkv = dims->n_heads_kv;
+  p.G = dims->n_heads_q / dims->n_heads_kv;
+  p.P = dims->prefix_len;
+  p.C = dims->chunk_len;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = (float)((double)dims->softmax_scale * 1.4426950408889634);
+  p.plan = plan_bwd(*dims);
+  const size_t nrow = (size_t)p.B * p.Hq * p.C;
+  float* ws_delta = static_cast<float*>(ws);
+  p.delta = delta ? delta : ws_delta;
+  if (p.plan.n_split > 1)
+    p.ws_dq = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(nrow * 4));
+  hipError_t e = launch_bwd(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "chunk_attn_bwd launch");
+  return PKA_OK;
+}
+
+static pka_status append_common(const pka_dims* dims, const void* k, const void* v,
+                                const pka_cache* cache, pka_stream_t stream, int want_type) {
+  g_last_error[0] = 0;
+  pka_status st;
+  if (!dims) return fail(PKA_ERR_NULL, "dims is NULL");
+  if (dims->batch < 1 || dims->n_heads_kv < 1)
+    return fail(PKA_ERR_DIMS, "batch and n_heads_kv must be >= 1");
+  if (dims->head_dim != 64 && dims->head_dim != 128)
+    return fail(PKA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", dims->head_dim);
+  if (dims->prefix_len < 0 || dims->chunk_len < 1)
+    return fail(PKA_ERR_DIMS, "prefix_len must be >= 0 and chunk_len >= 1");
+  if (dims->prefix_len > kMaxSeq - dims->chunk_len)
+    return fail(PKA_ERR_DIMS, "prefix_len + chunk_len exceeds 2^31 - 1");
+  if ((st = check_ptrs({k, v}, "k, v")) != PKA_OK) return st;
+  if ((st = check_cache(cache, dims, dims->prefix_len + dims->chunk_len, true)) != PKA_OK) return st;
+  if (cache->type != want_type)
+    return fail(PKA_ERR_UNSUPPORTED, "cache type %d does not match this append (%d)", cache->type,
+                want_type);
+  AppendParams p{};
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.ck = cache->k;
+  p.cv = cache->v;
+  p.cks = static_cast<uint16_t*>(cache->k_scale);
+  p.cvs = static_cast<uint16_t*>(cache->v_scale);
+  p.rows = (int64_t)dims->batch * dims->n_heads_kv * dims->chunk_len;
+  p.C = dims->chunk_len;
+  p.P = dims->prefix_len;
+  p.cap = cache->capacity;
+  p.D = dims->head_dim;
+  hipError_t e = launch_append(p, want_type, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+  return PKA_OK;
+}
+
+pka_status pka_kv_append_q8_0(const pka_dims* dims, const void* k, const void* v,
+                              const pka_cache* cache, pka_stream_t stream) {
+  return append_common(dims, k, v, cache, stream, PKA_CACHE_Q8_0);
+}
+pka_status pka_kv_append_f16(const pka_dims* dims, const void* k, const void* v,
+                             const pka_cache* cache, pka_stream_t stream) {
+  return append_common(dims, k, v, cache, stream, PKA_CACHE_F16);
+}
+pka_status pka_kv_append_bf16(const pka_dims* dims, const void* k, const void* v,
+                              const pka_cache* cache, pka_stream_t stream) {
+  return append_common(dims, k, v, cache, stream, PKA_CACHE_BF16);
+}
+
+pka_status pka_kv_dequant_q8_0(const pka_cache* cache, int32_t batch, int32_t n_heads_kv,
+                               int64_t row0, int64_t rows, float* out_f32, void* out_bf16,
+                               pka_stream_t stream) {
+  g_last_error[0] = 0;
+  if (!cache) return fail(PKA_ERR_NULL, "cache is NULL");
+  if (cache->type != PKA_CACHE_Q8_0) return fail(PKA_ERR_UNSUPPORTED, "cache is not q8_0");
+  if (cache->head_dim != 64 && cache->head_dim != 128)
+    return fail(PKA_ERR_UNSUPPORTED, "head_dim %d not supported", cache->head_dim);
+  if (batch < 1 || n_heads_kv < 1 || row0 < 0 || rows < 1)
+    return fail(PKA_ERR_DIMS, "batch, n_heads_kv, rows must be >= 1 and row0 >= 0");
+  if (row0 > cache->capacity - rows)
+    return fail(PKA_ERR_CAPACITY, "rows [%lld, %lld) exceed capacity %lld", (long long)row0,
+                (long long)(row0 + rows), (long long)cache->capacity);
+  pka_status st;
+  if ((st = check_ptrs({cache->k, cache->v, cache->k_scale, cache->v_scale, out_f32},
+                       "cache k, v, scales, out_f32")) != PKA_OK)
+    return st;
+  if (out_bf16 && !aligned16(out_bf16)) return fail(PKA_ERR_ALIGN, "out_bf16 not 16-byte aligned");
+  DequantParams p{};
+  p.ck = static_cast<const int8_t*>(cache->k);
+  p.cv = static_cast<const int8_t*>(cache->v);
+  p.cks = static_cast<const uint16_t*>(cache->k_scale);
+  p.cvs = static_cast<const uint16_t*>(cache->v_scale);
+  p.out_f32 = out_f32;
+  p.out_bf16 = static_cast<uint16_t*>(out_bf16);
+  p.BH = (int64_t)batch * n_heads_kv;
+  p.row0 = row0;
+  p.rows = rows;
+  p.cap = cache->capacity;
+  p.D = cache->head_dim;
+  hipError_t e = launch_dequant(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "kv_dequant_q8_0 launch");
+  return PKA_OK;
+}
+
+pka_status pka_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return PKA_OK;
+}
+
+pka_status pka_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& sl : g_prof) {
+    sl.used = 0;
+    sl.dropped = 0;
+  }
+  return PKA_OK;
+}
+
+pka_status pka_profile_read(int32_t kernel, double* total_ms, int64_t* launches,
+                            int64_t* dropped) {
+  g_last_error[0] = 0;
+  if (kernel < 0 || kernel >= PKA_KERNEL_COUNT)
+    return fail(PKA_ERR_DIMS, "unknown kernel id %d", kernel);
+  if (!total_ms || !launches) return fail(PKA_ERR_NULL, "total_ms / launches is NULL");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  ProfSlot& sl = g_prof[kernel];
+  double sum = 0.0;
+  for (int64_t i = 0; i < sl.used; ++i) {
+    hipError_t e = hipEventSynchronize(sl.end[i]);
+    if (e != hipSuccess) return hip_fail(e, "profile event sync");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, sl.begin[i], sl.end[i]);
+    if (e != hipSuccess) return hip_fail(e, "profile elapsed time");
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = sl.used;
+  if (dropped) *dropped = sl.dropped;
+  return PKA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Device helpers for gfx950 (CDNA4): MFMA wrappers, bf16/f16/q8_0 conversion,
+// LDS layouts and the XCD-aware workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pka_internal.hpp"
+
+namespace pka {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16). Lane l supplies A row l%32 and
+// B column l%32, each with the 8 k-values (l/32)*8 .. +7 of the 16-wide k-step.
+// The result holds column l%32 and rows (r/4)*8 + (l/32)*4 + r%4, r = 0..15.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b,
+                                         const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Within a 32-row block of an MFMA result, lane half hf holds rows
+// (r/4)*8 + hf*4 + r%4. Feeding registers 8s..8s+7 (k-step s) back as an operand
+// whose lane half hf supplies k-values hf*8 + e makes k-position s*16 + hf*8 + e
+// stand for row swap23(that position): bits 2 and 3 of the index exchanged. The
+// other operand is staged in LDS with the same permutation (an involution).
+__device__ __forceinline__ int swap23(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Two floats -> packed bf16 pair (round to nearest even), a in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Eight consecutive values of one key row, as loaded from HBM before conversion.
+// Cache rows of F16/BF16 and chunk rows: 16 bytes. Q8_0 cache rows: 8 code bytes in
+// .x/.y and the block's fp16 scale in .z.
+struct RawRow8 {
+  u32x4 w;
+};
+
+enum : int { kF16 = PKA_CACHE_F16, kBF16 = PKA_CACHE_BF16, kQ8 = PKA_CACHE_Q8_0 };
+
+// Load 8 values (d0 .. d0+7) of key row j of the virtual key sequence
+// [cache rows 0..P-1 ; chunk rows 0..C-1] of one (window, KV head).
+// Returns true if the row is a cache row (needs conversion), false for a chunk row
+// or a zero row beyond the sequence.
+template <int CT, int D>
+__device__ __forceinline__ bool load_row8(RawRow8& r, const void* cache_base,
+                                          const uint16_t* cache_scale,
+                                          const uint16_t* chunk_base, int64_t P,
+                                          int64_t C, int64_t j, int d0) {
+  if (j < P) {
+    if constexpr (CT == kQ8) {
+      const int8_t* src = static_cast<const int8_t*>(cache_base) + j * D + d0;
+      u32x2 c = *reinterpret_cast<const u32x2*>(src);
+      uint32_t s = cache_scale[j * (D / 32) + (d0 >> 5)];
+      r.w = u32x4{c.x, c.y, s, 0u};
+    } else {
+      const uint16_t* src = static_cast<const uint16_t*>(cache_base) + j * D + d0;
+      r.w = *reinterpret_cast<const u32x4*>(src);
+    }
+    return true;
+  }
+  if (j < P + C) {
+    r.w = *reinterpret_cast<const u32x4*>(chunk_base + (j - P) * D + d0);
+  } else {
+    r.w = u32x4{0u, 0u, 0u, 0u};
+  }
+  return false;
+}
+
+// Raw row -> 8 bf16 values packed in 4 dwords (element 2i in the low half of .i).
+template <int CT>
+__device__ __forceinline__ u32x4 to_bf16x8(const RawRow8& r, bool is_cache) {
+  if (!is_cache || CT == kBF16) return r.w;
+  if constexpr (CT == kF16) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = r.w[i];
+      o[i] = pack_bf16(f16_to_f32(w & 0xffffu), f16_to_f32(w >> 16));
+    }
+    return o;
+  } else {
+    const float d = f16_to_f32(r.w.z);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = (i < 2) ? r.w.x : r.w.y;
+      const int sh = (i & 1) * 16;
+      const float a = d * (float)(int8_t)((w >> sh) & 0xff);
+      const float b = d * (float)(int8_t)((w >> (sh + 8)) & 0xff);
+      o[i] = pack_bf16(a, b);
+    }
+    return o;
+  }
+}
+
+// Workgroup order: hardware dispatches workgroup i to XCD i % 8. Renumber so each
+// XCD receives a contiguous range of logical ids; neighbouring logical ids read the
+// same K/V tiles and so share that XCD's L2.
+__device__ __forceinline__ int xcd_logical_id(int i, int nblk) {
+  const int q = nblk / kNumXCDs;
+  const int rem = nblk % kNumXCDs;
+  const int x = i % kNumXCDs;
+  const int k = i / kNumXCDs;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
+__device__ __forceinline__ float wave_xor32(float v) {
+  return __shfl_xor(v, 32, 64);
+}
+
+}  // namespace pka

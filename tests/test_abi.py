@@ -1,0 +1,192 @@
+"""C-ABI tests that need no GPU: the library loads, exports every entry point that
+include/pka.h declares, and refuses bad arguments on the host before any HIP call
+(so nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pka.h")
+LIB = os.path.join(ROOT, "prefix_kv_attention_amd", "libpka.so")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pka_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def pka():
+    if not os.path.exists(LIB):
+        pytest.fail("libpka.so is not built (python prefix_kv_attention_amd/build.py)")
+    import prefix_kv_attention_amd as m
+    return m
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("pka_chunk_attn_fwd", "pka_chunk_attn_bwd", "pka_kv_append_q8_0",
+              "pka_kv_append_f16", "pka_kv_append_bf16", "pka_kv_dequant_q8_0",
+              "pka_fwd_workspace_bytes", "pka_bwd_workspace_bytes", "pka_status_string",
+              "pka_last_error", "pka_profile_enable", "pka_profile_reset", "pka_profile_read"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(pka):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pka_[a-z0-9_]+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(pka.lib, n)      # resolvable through ctypes as well
+
+
+# Fake, 16-byte aligned device addresses: every call below must fail validation,
+# so none of them is ever dereferenced.
+A = 0x7F0000000000
+MIS = A + 8
+
+
+def dims(pka, **kw):
+    d = dict(batch=1, n_heads_q=4, n_heads_kv=2, head_dim=128, prefix_len=256,
+             chunk_len=64, softmax_scale=0.125)
+    d.update(kw)
+    return pka.make_dims(**d)
+
+
+def cache(pka, **kw):
+    c = dict(type=pka.CACHE_F16, head_dim=128, capacity=512, k=A, v=A, k_scale=None,
+             v_scale=None)
+    c.update(kw)
+    return pka.CacheDesc(c["type"], c["head_dim"], c["capacity"], c["k"], c["v"],
+                         c["k_scale"], c["v_scale"])
+
+
+def fwd(pka, d, c, ptrs=None, ws=None, ws_bytes=0):
+    p = dict(q=A, k=A, v=A, o=A, lse=A)
+    p.update(ptrs or {})
+    st = pka.lib.pka_chunk_attn_fwd(ctypes.byref(d) if d is not None else None, p["q"], p["k"],
+                                    p["v"], ctypes.byref(c) if c is not None else None,
+                                    p["o"], p["lse"], ws, ws_bytes, None)
+    return st, pka.lib.pka_last_error().decode()
+
+
+def bwd(pka, d, c, ptrs=None, ws=A, ws_bytes=1 << 40, delta=None):
+    p = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A)
+    p.update(ptrs or {})
+    st = pka.lib.pka_chunk_attn_bwd(ctypes.byref(d), p["q"], p["k"], p["v"], ctypes.byref(c),
+                                    p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                                    delta, ws, ws_bytes, None)
+    return st, pka.lib.pka_last_error().decode()
+
+
+CASES_FWD = [
+    ("null dims", lambda pka: (None, cache(pka), None), 1),
+    ("hq % hkv", lambda pka: (dims(pka, n_heads_q=5), cache(pka), None), 2),
+    ("batch 0", lambda pka: (dims(pka, batch=0), cache(pka), None), 2),
+    ("head_dim 96", lambda pka: (dims(pka, head_dim=96), cache(pka, head_dim=96), None), 3),
+    ("chunk 0", lambda pka: (dims(pka, chunk_len=0), cache(pka), None), 2),
+    ("chunk too long", lambda pka: (dims(pka, chunk_len=65537), cache(pka), None), 2),
+    ("negative prefix", lambda pka: (dims(pka, prefix_len=-1), cache(pka), None), 2),
+    ("seq overflow", lambda pka: (dims(pka, prefix_len=2**31 - 10), cache(pka), None), 2),
+    ("scale 0", lambda pka: (dims(pka, softmax_scale=0.0), cache(pka), None), 2),
+    ("scale nan", lambda pka: (dims(pka, softmax_scale=float("nan")), cache(pka), None), 2),
+    ("null q", lambda pka: (dims(pka), cache(pka), {"q": None}), 1),
+    ("null lse", lambda pka: (dims(pka), cache(pka), {"lse": None}), 1),
+    ("misaligned o", lambda pka: (dims(pka), cache(pka), {"o": MIS}), 5),
+    ("null cache", lambda pka: (dims(pka), None, None), 1),
+    ("cache type 9", lambda pka: (dims(pka), cache(pka, type=9), None), 3),
+    ("cache head_dim", lambda pka: (dims(pka), cache(pka, head_dim=64), None), 2),
+    ("capacity < P", lambda pka: (dims(pka), cache(pka, capacity=255), None), 4),
+    ("null cache k", lambda pka: (dims(pka), cache(pka, k=None), None), 1),
+    ("misaligned cache v", lambda pka: (dims(pka), cache(pka, v=MIS), None), 5),
+    ("q8_0 no scales", lambda pka: (dims(pka), cache(pka, type=2), None), 1),
+    ("q8_0 misaligned scale", lambda pka: (dims(pka), cache(pka, type=2, k_scale=A,
+                                                             v_scale=MIS), None), 5),
+]
+
+
+@pytest.mark.parametrize("name,make,want", CASES_FWD, ids=[c[0] for c in CASES_FWD])
+def test_fwd_validation(pka, name, make, want):
+    d, c, ptrs = make(pka)
+    st, msg = fwd(pka, d, c, ptrs)
+    assert st == want, (name, st, msg)
+    assert msg
+
+
+def test_fwd_workspace_required_when_split(pka):
+    d = dims(pka, batch=1, n_heads_q=2, n_heads_kv=1, prefix_len=16384, chunk_len=64)
+    need = pka.fwd_workspace_bytes(d)
+    assert need > 0
+    st, msg = fwd(pka, d, cache(pka, capacity=20000))
+    assert st == 6 and "workspace" in msg
+    st, _ = fwd(pka, d, cache(pka, capacity=20000), ws=A, ws_bytes=need - 1)
+    assert st == 6
+    st, _ = fwd(pka, d, cache(pka, capacity=20000), ws=MIS, ws_bytes=need)
+    assert st == 5
+
+
+def test_bwd_validation(pka):
+    d = dims(pka)
+    need = pka.bwd_workspace_bytes(d)
+    assert need >= 1 * 4 * 64 * 4
+    assert bwd(pka, d, cache(pka), ws=None)[0] == 6
+    assert bwd(pka, d, cache(pka), ws=A, ws_bytes=need - 1)[0] == 6
+    assert bwd(pka, d, cache(pka), ptrs={"do": None})[0] == 1
+    assert bwd(pka, d, cache(pka), ptrs={"dk": MIS})[0] == 5
+    assert bwd(pka, d, cache(pka), delta=MIS)[0] == 5
+    assert bwd(pka, d, cache(pka, capacity=100))[0] == 4
+    assert bwd(pka, dims(pka, n_heads_kv=3), cache(pka))[0] == 2
+
+
+def test_append_validation(pka):
+    lib = pka.lib
+    d = dims(pka, prefix_len=500, chunk_len=64)
+    c = cache(pka, capacity=563)                       # P + C = 564 > capacity
+    assert lib.pka_kv_append_f16(ctypes.byref(d), A, A, ctypes.byref(c), None) == 4
+    c = cache(pka, capacity=600, type=pka.CACHE_F16)
+    assert lib.pka_kv_append_q8_0(ctypes.byref(d), A, A, ctypes.byref(c), None) == 3
+    assert lib.pka_kv_append_bf16(ctypes.byref(d), A, A, ctypes.byref(c), None) == 3
+    assert lib.pka_kv_append_f16(ctypes.byref(d), None, A, ctypes.byref(c), None) == 1
+    assert lib.pka_kv_append_f16(ctypes.byref(d), A, MIS, ctypes.byref(c), None) == 5
+    cq = cache(pka, capacity=600, type=pka.CACHE_Q8_0)
+    assert lib.pka_kv_append_q8_0(ctypes.byref(d), A, A, ctypes.byref(cq), None) == 1
+    assert lib.pka_kv_append_f16(None, A, A, ctypes.byref(c), None) == 1
+
+
+def test_dequant_validation(pka):
+    lib = pka.lib
+    cq = cache(pka, capacity=100, type=pka.CACHE_Q8_0, k_scale=A, v_scale=A)
+    assert lib.pka_kv_dequant_q8_0(ctypes.byref(cq), 1, 1, 50, 51, A, None, None) == 4
+    assert lib.pka_kv_dequant_q8_0(ctypes.byref(cq), 1, 1, 0, 0, A, None, None) == 2
+    assert lib.pka_kv_dequant_q8_0(ctypes.byref(cq), 1, 1, 0, 10, None, None, None) == 1
+    assert lib.pka_kv_dequant_q8_0(ctypes.byref(cq), 1, 1, 0, 10, A, MIS, None) == 5
+    cf = cache(pka, capacity=100, type=pka.CACHE_F16)
+    assert lib.pka_kv_dequant_q8_0(ctypes.byref(cf), 1, 1, 0, 10, A, None, None) == 3
+
+
+def test_status_strings_and_profile_ids(pka):
+    for st in range(8):
+        assert pka.lib.pka_status_string(st)
+    ms, n, dr = ctypes.c_double(), ctypes.c_int64(), ctypes.c_int64()
+    assert pka.lib.pka_profile_read(99, ctypes.byref(ms), ctypes.byref(n), ctypes.byref(dr)) == 2
+    assert pka.lib.pka_profile_read(0, None, None, None) == 1
+
+
+def test_workspace_plan(pka):
+    # The headline shape fills the chip without splitting the prefix.
+    assert pka.fwd_workspace_bytes(dims(pka, batch=4, n_heads_q=32, n_heads_kv=8,
+                                        prefix_len=16384, chunk_len=512)) == 0
+    # Few (window, KV head) units: split, with partials sized by the split count.
+    d3 = dims(pka, batch=2, n_heads_q=12, n_heads_kv=2, prefix_len=16384, chunk_len=512)
+    nrow = 2 * 12 * 512
+    ws = pka.fwd_workspace_bytes(d3)
+    assert ws >= 2 * nrow * 129 * 4 and ws % 256 == 0
+    assert pka.bwd_workspace_bytes(d3) >= nrow * 4 + 2 * nrow * 128 * 4
+    # invalid dims -> 0
+    assert pka.fwd_workspace_bytes(dims(pka, head_dim=80)) == 0
