@@ -1,0 +1,217 @@
+"""Benchmark of the prefix-KV chunk attention hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+chunk_attn_fwd, chunk_attn_bwd (delta, dQ, chunk-only dK/dV) and the append of the
+chunk's K/V to the cache, on the 8B-like workload by default (4 windows, 32 query /
+8 KV heads, head_dim 128, bf16 prefix cache, P = 16384, C = 512).
+
+Prints one JSON line. `value` is fwd+bwd algorithmic TFLOP/s of the whole step
+(forward: 2 contractions over every allowed (query, key) pair; backward: 3 over
+prefix pairs and 5 over chunk pairs; S recompute counted, avoided prefix dK/dV
+not). `roofline` is for the dominant kernel (bwd_dq), timed live with HIP events
+around each of its launches inside the timed region. `cpu_baseline` times the
+fp64 oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "chunk attn fwd+bwd TFLOP/s + prefix-KV GB/s (%roofline) at P=16384,C=512"
+
+
+def pairs(w):
+    prefix = w.chunk_len * w.prefix_len
+    chunk = w.chunk_len * (w.chunk_len + 1) // 2
+    return prefix, chunk
+
+
+def flops(w):
+    """Algorithmic FLOPs of forward and backward."""
+    pp, cp = pairs(w)
+    unit = 2 * w.batch * w.n_heads_q * w.head_dim   # FLOPs of one contraction per pair
+    fwd = 2 * unit * (pp + cp)
+    bwd = unit * (3 * pp + 5 * cp)
+    dq = 3 * unit * (pp + cp)                       # S, dP, dQ over every pair
+    return fwd, bwd, dq
+
+
+def prefix_bytes(w):
+    rows = w.batch * w.n_heads_kv * w.prefix_len
+    if w.cache_type == "q8_0":
+        per_row = w.head_dim + 2 * (w.head_dim // 32)
+    else:
+        per_row = 2 * w.head_dim
+    return 2 * rows * per_row   # K and V
+
+
+def read_traffic(kernel_name):
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    try:
+        import hashlib
+        src = open(os.path.join(ROOT, "prefix_kv_attention_amd", "csrc",
+                                vals["source_file"]), "rb").read()
+        if hashlib.sha256(src).hexdigest()[:16] != vals["source_sha256_16"]:
+            return None
+        return float(vals["bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def cpu_baseline(w, inputs, budget_s=15.0):
+    """Time the fp64 oracle on (window, KV head) groups until ~budget_s is spent."""
+    import numpy as np
+    import oracle
+    from oracle.cache import from_torch_bf16
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    G = w.group
+    sc = w.softmax_scale
+    done, spent, fl = 0, 0.0, 0.0
+    fwd_f, bwd_f, _ = flops(w)
+    per_group = (fwd_f + bwd_f) / (w.batch * w.n_heads_kv)
+    groups = [(b, kv) for b in range(w.batch) for kv in range(w.n_heads_kv)]
+    for b, kv in groups:
+        hs = slice(kv * G, (kv + 1) * G)
+        f = lambda t: from_torch_bf16(t).astype(np.float64)
+        kp = oracle.build_prefix(from_torch_bf16(inputs["kp"][b, kv]), w.cache_type)["values"]
+        vp = oracle.build_prefix(from_torch_bf16(inputs["vp"][b, kv]), w.cache_type)["values"]
+        q, kc, vc, do = f(inputs["q"][b, hs]), f(inputs["kc"][b, kv]), f(inputs["vc"][b, kv]), \
+            f(inputs["do"][b, hs])
+        t0 = time.perf_counter()
+        oracle.group_fwd(q, kc, vc, kp, vp, sc)
+        oracle.group_bwd(q, kc, vc, kp, vp, sc, do)
+        spent += time.perf_counter() - t0
+        done += 1
+        fl += per_group
+        if spent >= budget_s:
+            break
+    return {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(groups)} (window, KV head) groups of {w.name} "
+                      f"({G} query heads x {w.chunk_len} rows vs {w.prefix_len + w.chunk_len} "
+                      f"keys each), fp64 forward + backward, {spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8b-16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the step without the per-kernel HIP events")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the hot path here is one GPU's share at its real "
+              "shape and has no cross-GPU step; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import prefix_kv_attention_amd as pka
+    import synthetic
+
+    w = synthetic.WORKLOAD_BY_NAME[args.workload]
+    dev = "cuda:0"
+    inputs = synthetic.make_inputs(w)
+    d = {k: v.to(dev) for k, v in inputs.items()}
+    B, Hq, Hkv, D, P, C = w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, w.prefix_len, w.chunk_len
+    cache = pka.PrefixCache.empty(w.cache_type, B, Hkv, P + C, D, dev)
+    pka.kv_append(d["kp"], d["vp"], cache, 0)
+    del d["kp"], d["vp"]
+    q, kc, vc, do = d["q"], d["kc"], d["vc"], d["do"]
+    sc = w.softmax_scale
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(kc), torch.empty_like(vc)
+    dims = pka.make_dims(B, Hq, Hkv, D, P, C, sc)
+    wsf = pka.fwd_workspace_bytes(dims)
+    wsb = pka.bwd_workspace_bytes(dims)
+    ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev) if wsf else None
+    ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def step():
+        pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
+        pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b)
+        pka.kv_append(kc, vc, cache, P)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    kernel_events = not args.no_kernel_events
+    pka.profile_reset()
+    pka.profile_enable(kernel_events)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pka.profile_enable(False)
+
+    ms_step = elapsed * 1e3 / args.steps
+    fwd_f, bwd_f, dq_f = flops(w)
+    tflops = (fwd_f + bwd_f) / (ms_step * 1e-3) / 1e12
+    pbytes = prefix_bytes(w)
+    prefix_gbs = 2 * pbytes / (ms_step * 1e-3) / 1e9
+
+    kernels = {}
+    if kernel_events:
+        for name in ("fwd", "fwd_combine", "bwd_prep", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce",
+                     "append"):
+            tot, n, _ = pka.profile_read(name)
+            if n:
+                kernels[name] = round(tot / n, 5)
+    roofline = None
+    if "bwd_dq" in kernels:
+        achieved = dq_f / (kernels["bwd_dq"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "bwd_dq", "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                    "traffic": read_traffic("bwd_dq"),
+                    "flop_per_launch": dq_f, "avg_launch_ms": kernels["bwd_dq"]}
+    out = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_heads_q": Hq, "n_heads_kv": Hkv,
+                   "head_dim": D, "prefix_len": P, "chunk_len": C, "cache": w.cache_type,
+                   "step": "chunk_attn_fwd + chunk_attn_bwd + kv_append"},
+        "prefix_kv_gbs": round(prefix_gbs, 1),
+        "prefix_kv_hbm_frac": round(prefix_gbs / PEAK_HBM_GBS, 4),
+        "mfma_frac_step": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "kernel_ms": kernels,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
