@@ -122,7 +122,21 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the step without the per-kernel HIP events")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (scales the HBM "
+                         "byte counters of a profiler run)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written":
+                          dst.numel() * 4, "launches": 3}), flush=True)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the hot path here is one GPU's share at its real "

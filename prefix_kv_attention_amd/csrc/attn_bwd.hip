@@ -9,40 +9,32 @@
 //
 // Kernels, in launch order on the caller's stream:
 //  1. bwd_prep:  delta_i = sum_d dO_id * O_id from the stored bf16 O.
-//  2. bwd_dq:    per 128 packed query rows (GQA packing as in the forward), stream
-//                the key tiles: S^T = K Q^T, dP^T = V dO^T (MFMA bf16),
+//  2. bwd_dq:    per 256 packed query rows (GQA packing as in the forward), stream
+//                the key tiles: S^T = K Q^T and dP^T = V dO^T (MFMA bf16),
 //                P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - delta) in
-//                registers, dQ^T += K^T dS^T (MFMA, dS^T registers reused as the B
-//                operand). Split over key tiles like the forward when the units
-//                are too few; fp32 partials are summed by bwd_dq_reduce in a fixed
-//                order.
-//  3. bwd_dkdv:  per 128 chunk keys of one (window, KV head), stream the packed
-//                query rows of all G heads that can see them (token >= key):
-//                S = Q K^T and dP = dO V^T with keys as MFMA columns, then
-//                dV^T += dO^T P and dK^T += Q^T dS; the sum over the G heads of a
-//                KV head falls out of the packing. No atomics: every output element
-//                is owned by one lane.
+//                registers, dQ^T += K^T dS^T with the dS^T registers as the B operand
+//                and K^T read from the row-major K tile by the transposing LDS read.
+//                Split over key tiles like the forward when the units are too few;
+//                fp32 partials are summed by bwd_dq_reduce in a fixed order.
+//  3. bwd_dkdv:  per 64 chunk keys of one (window, KV head), stream the packed
+//                query rows of all G heads that can see them (token >= key) in tiles
+//                of 64: S = Q K^T and dP = dO V^T with keys as MFMA columns, then
+//                dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposing reads).
+//                Waves 0-1 take the first 32 rows of every tile and waves 2-3 the
+//                second 32; the two partial sums are added through LDS at the end.
+//                The sum over the G heads of a KV head falls out of the packing.
+// No atomics anywhere: every output element is owned by one lane (deterministic).
 #include "pka_device.hpp"
 
 namespace pka {
 namespace {
 
 constexpr int BN = kKeysPerTile;
+constexpr int NW = kWavesPerBlock;
+constexpr int NTHR = 64 * NW;
 
 __device__ __forceinline__ uint32_t elem16(const u32x4& w, int e) {
   return (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-}
-
-// 4 rows x 8 values -> transposed LDS rows dst[(d0+e)*stride + pos .. pos+3].
-__device__ __forceinline__ void store_transposed(uint16_t* dst, int stride, int d0,
-                                                 int pos, const u32x4 (&w)[4]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    u32x2 pr;
-    pr.x = elem16(w[0], e) | (elem16(w[1], e) << 16);
-    pr.y = elem16(w[2], e) | (elem16(w[3], e) << 16);
-    *reinterpret_cast<u32x2*>(&dst[(d0 + e) * stride + pos]) = pr;
-  }
 }
 
 template <int D>
@@ -65,53 +57,100 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   if (row < nrow && c8 == 0) p.delta[row] = s;
 }
 
+// Raw rows of one staging task: 4 rows x 8 values, as loaded from HBM.
+struct Task4 {
+  u32x4 w[4];
+  bool cache[4];
+};
+
+template <int CT, int D>
+__device__ __forceinline__ void load_fast(Task4& t, const char* base, const char* sbase,
+                                          int r0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (CT == kQ8) {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base + (r0 + i) * D + d0);
+      const uint32_t s =
+          *reinterpret_cast<const uint16_t*>(sbase + ((r0 + i) * (D / 32) + (d0 >> 5)) * 2);
+      t.w[i] = u32x4{c.x, c.y, s, 0u};
+    } else {
+      t.w[i] = *reinterpret_cast<const u32x4*>(base + ((r0 + i) * D + d0) * 2);
+    }
+    t.cache[i] = true;
+  }
+}
+
+template <int CT, int D>
+__device__ __forceinline__ void load_general(Task4& t, const void* cache_base,
+                                             const uint16_t* cache_scale,
+                                             const uint16_t* chunk_base, int64_t P, int64_t C,
+                                             int64_t j0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    RawRow8 r;
+    t.cache[i] = load_row8<CT, D>(r, cache_base, cache_scale, chunk_base, P, C, j0 + i, d0);
+    t.w[i] = r.w;
+  }
+}
+
+template <int CT, int S>
+__device__ __forceinline__ void store_rows(uint16_t* tile, const Task4& t, int r0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    RawRow8 r;
+    r.w = t.w[i];
+    *reinterpret_cast<u32x4*>(&tile[prow(r0 + i) * S + d0]) = to_bf16x8<CT>(r, t.cache[i]);
+  }
+}
+
 template <int D>
-struct DqSmem {
-  static constexpr int KS = D + 8;
-  static constexpr int KT = BN + 8;
-  uint16_t k[BN * KS];
-  uint16_t kt[D * KT];
-  uint16_t v[BN * KS];
+struct DqLds {
+  static constexpr int S = D + 8;
+  uint16_t k[2][BN * S];
+  uint16_t v[2][BN * S];
 };
 
 template <int D, int CT>
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
-  __shared__ DqSmem<D> sm;
-  constexpr int KS = DqSmem<D>::KS;
-  constexpr int KT = DqSmem<D>::KT;
+__global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __align__(16) DqLds<D> sm;
+  constexpr int S = DqLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int NTASK = (BN / 4) * CH;
+  constexpr int NT = 16 * CH;
+  constexpr int ESZ = (CT == kQ8) ? 1 : 2;
+  constexpr int ROWS = 32 * NW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int n_rb = p.plan.n_rb, S = p.plan.n_split;
+  const int n_rb = p.plan.n_rb, SPL = p.plan.n_split;
   const int L = xcd_logical_id(blockIdx.x, p.plan.nblk);
   const int rb = L % n_rb;
-  const int split = (L / n_rb) % S;
-  const int grp = L / (n_rb * S);
+  const int split = (L / n_rb) % SPL;
+  const int grp = L / (n_rb * SPL);
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int G = p.G;
-  const int64_t C = p.C, P = p.P;
-  const int rows = G * (int)C;
+  const int C = (int)p.C;
+  const int P = (int)p.P;
+  const int rows = G * C;
 
-  const int r = rb * kRowsPerBlock + wave * 32 + l32;
+  const int r = rb * ROWS + wave * 32 + l32;
   const bool row_ok = r < rows;
   const int rr = row_ok ? r : rows - 1;
   const int t = rr / G;
   const int h = kv * G + (rr - t * G);
   const int64_t qrow = ((int64_t)b * p.Hq + h) * C + t;
 
-  const int r_first = rb * kRowsPerBlock;
-  const int r_last = min(rows - 1, r_first + kRowsPerBlock - 1);
+  const int r_first = rb * ROWS;
+  const int r_last = min(rows - 1, r_first + ROWS - 1);
   const int t_min = r_first / G, t_max = r_last / G;
-  const int64_t key_end = P + t_max + 1;
-  const int n_tiles = (int)((key_end + BN - 1) / BN);
-  const int tb = (int)((int64_t)split * n_tiles / S);
-  const int te = (int)((int64_t)(split + 1) * n_tiles / S);
+  const int key_end = P + t_max + 1;
+  const int n_tiles = (key_end + BN - 1) / BN;
+  const int tb = (int)((int64_t)split * n_tiles / SPL);
+  const int te = (int)((int64_t)(split + 1) * n_tiles / SPL);
+  const int n_fast = P / BN;
 
   bf16x8 qreg[NKS], oreg[NKS];
   {
@@ -127,100 +166,95 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdParams p) {
   const float lse2 = p.lse[qrow] * kLog2e;
   const float dlt = p.delta[qrow];
 
+  const bool stage_k = tid < NT;
+  const bool stage_v = tid >= 256 && tid < 256 + NT;
+  const bool stager = stage_k || stage_v;
+  const int task = stage_k ? tid : tid - 256;
+  const int tr0 = (task / CH) * 4, td0 = (task % CH) * 8;
+
   const int64_t bh = (int64_t)b * p.Hkv + kv;
   const int64_t cap = p.cache.cap;
-  const void* ck;
-  const void* cv;
-  if constexpr (CT == kQ8) {
-    ck = static_cast<const int8_t*>(p.cache.k) + bh * cap * D;
-    cv = static_cast<const int8_t*>(p.cache.v) + bh * cap * D;
-  } else {
-    ck = static_cast<const uint16_t*>(p.cache.k) + bh * cap * D;
-    cv = static_cast<const uint16_t*>(p.cache.v) + bh * cap * D;
-  }
-  const uint16_t* cks = (CT == kQ8) ? p.cache.ks + bh * cap * (D / 32) : nullptr;
-  const uint16_t* cvs = (CT == kQ8) ? p.cache.vs + bh * cap * (D / 32) : nullptr;
-  const uint16_t* kcb = p.kc + bh * C * D;
-  const uint16_t* vcb = p.vc + bh * C * D;
+  const char* cbase = static_cast<const char*>(stage_k ? p.cache.k : p.cache.v) + bh * cap * D * ESZ;
+  const uint16_t* cscale = (CT == kQ8) ? (stage_k ? p.cache.ks : p.cache.vs) + bh * cap * (D / 32)
+                                       : nullptr;
+  const uint16_t* chunk = (stage_k ? p.kc : p.vc) + bh * (int64_t)C * D;
 
-  const bool has_task = tid < NTASK;
-  const int kg = tid / CH, dg = tid % CH;
-  RawRow8 rk[4], rv[4];
-  bool ik[4], iv[4];
+  Task4 raw;
   auto issue = [&](int tile) {
-    const int64_t j0 = (int64_t)tile * BN + kg * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ik[i] = load_row8<CT, D>(rk[i], ck, cks, kcb, P, C, j0 + i, dg * 8);
-      iv[i] = load_row8<CT, D>(rv[i], cv, cvs, vcb, P, C, j0 + i, dg * 8);
+    if (tile < n_fast) {
+      load_fast<CT, D>(raw, cbase + (int64_t)tile * BN * D * ESZ,
+                       reinterpret_cast<const char*>(cscale + (int64_t)tile * BN * (D / 32)),
+                       tr0, td0);
+    } else {
+      load_general<CT, D>(raw, cbase, cscale, chunk, P, C, (int64_t)tile * BN + tr0, td0);
     }
   };
-  auto stage = [&]() {
-    u32x4 w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      w[i] = to_bf16x8<CT>(rk[i], ik[i]);
-      *reinterpret_cast<u32x4*>(&sm.k[(kg * 4 + i) * KS + dg * 8]) = w[i];
-      *reinterpret_cast<u32x4*>(&sm.v[(kg * 4 + i) * KS + dg * 8]) = to_bf16x8<CT>(rv[i], iv[i]);
-    }
-    store_transposed(sm.kt, KT, dg * 8, swap23(kg * 4), w);
+  auto stage = [&](int buf) {
+    store_rows<CT, S>(stage_k ? sm.k[buf] : sm.v[buf], raw, tr0, td0);
   };
+
+  const int k_off = prow(l32) * S + hf * 8;
+  const int t_off = tr_lane_offset<S>(lane);
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  const int64_t lim = P + t;
+  const int lim = P + t;
 
-  if (tb < te && has_task) issue(tb);
+  if (tb < te) {
+    if (stager) {
+      issue(tb);
+      stage(0);
+      if (tb + 1 < te) issue(tb + 1);
+    }
+    __syncthreads();
+  }
   for (int tile = tb; tile < te; ++tile) {
-    __syncthreads();
-    if (has_task) stage();
-    __syncthreads();
-    if (tile + 1 < te && has_task) issue(tile + 1);
-
-    f32x16 st[2], dpt[2];
+    const int cur = (tile - tb) & 1;
+    const uint16_t* kt = sm.k[cur];
+    const uint16_t* vt = sm.v[cur];
+    const int kbase = tile * BN;
+    const bool masked = kbase + BN - 1 > P + t_min;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
-      dpt[kb] = f32x16{};
+      f32x16 st = f32x16{}, dpt = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const int off = (kb * 32 + l32) * KS + ks * 16 + hf * 8;
-        st[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.k[off]), qreg[ks], st[kb]);
-        dpt[kb] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.v[off]), oreg[ks], dpt[kb]);
+        const int off = k_off + kb * 32 * S + ks * 16;
+        st = mfma32(*reinterpret_cast<const bf16x8*>(&kt[off]), qreg[ks], st);
+        dpt = mfma32(*reinterpret_cast<const bf16x8*>(&vt[off]), oreg[ks], dpt);
       }
-    }
-    const int64_t kbase = (int64_t)tile * BN;
-    if (kbase + BN - 1 > P + t_min) {
+      if (masked) {
+        const int rel = lim - kbase - hf * 4;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = kbase + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          if (key > lim) st[kb][i] = -INFINITY;
-        }
-    }
-    bf16x8 dsb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > rel) st[i] = -INFINITY;
+      }
+      bf16x8 dsb[2];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -lse2));
-        dsb[kb * 2 + (i >> 3)][i & 7] = (__bf16)(pv * (dpt[kb][i] - dlt));
+        const float pv = __builtin_amdgcn_exp2f(fmaf(st[i], c, -lse2));
+        dsb[i >> 3][i & 7] = (__bf16)(pv * (dpt[i] - dlt));
       }
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&sm.kt[(db * 32 + l32) * KT + kk * 16 + hf * 8]);
-        acc[db] = mfma32(a, dsb[kk], acc[db]);
+        for (int s = 0; s < 2; ++s)
+          acc[db] = mfma32(lds_tr_operand<S>(kt, t_off, kb * 32 + s * 16, db * 32), dsb[s], acc[db]);
+    }
+
+    if (tile + 1 < te) {
+      if (stager) {
+        stage(cur ^ 1);
+        if (tile + 2 < te) issue(tile + 2);
       }
+      __syncthreads();
+    }
   }
 
   if (!row_ok) return;
   const float sc = p.scale;
-  if (S == 1) {
+  if (SPL == 1) {
     uint16_t* op = p.dq + qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -270,45 +304,51 @@ __global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(BwdParams p) {
   *reinterpret_cast<u32x4*>(p.dq + row * D + c8 * 8) = out;
 }
 
-constexpr int BQ = 32;  // packed query rows per dK/dV step
+// ------------------------------------------------------------------ dK / dV
+constexpr int BQ = 64;                      // packed query rows per step
+constexpr int KB = kDkvKeysPerBlock;        // chunk keys per workgroup (64)
 
 template <int D>
-struct DkvSmem {
-  static constexpr int QS = D + 8;
-  static constexpr int QT = BQ + 8;
-  uint16_t q[BQ * QS];
-  uint16_t g[BQ * QS];   // dO
-  uint16_t qt[D * QT];
-  uint16_t gt[D * QT];
-  float lse2[BQ];
-  float dlt[BQ];
-  int tok[BQ];
+struct DkvLds {
+  static constexpr int S = D + 8;
+  union {
+    struct {
+      uint16_t q[2][BQ * S];
+      uint16_t g[2][BQ * S];   // dO
+    } t;
+    float red[2][32 * D * 2];  // partial dK^T, dV^T of waves 2-3 (fp32)
+  } u;
+  float lse2[2][BQ];
+  float dlt[2][BQ];
+  int tok[2][BQ];
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
-  __shared__ DkvSmem<D> sm;
-  constexpr int QS = DkvSmem<D>::QS;
-  constexpr int QT = DkvSmem<D>::QT;
+  __shared__ __align__(16) DkvLds<D> sm;
+  constexpr int S = DkvLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int NT = (BQ / 4) * CH;  // staging tasks per tensor (<= 128)
+  constexpr int NT = (BQ / 4) * CH;   // staging tasks per tensor (<= 256)
+  static_assert(KB == 64, "two key blocks of 32 per workgroup");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int64_t C = p.C;
+  const int kw = wave & 1;       // key block of this wave
+  const int qb = wave >> 1;      // query half of every tile this wave takes
+  const int C = (int)p.C;
   const int G = p.G;
-  const int rows = G * (int)C;
-  const int nkb = (int)((C + kDkvKeysPerBlock - 1) / kDkvKeysPerBlock);
+  const int rows = G * C;
+  const int nkb = (C + KB - 1) / KB;
   const int L = blockIdx.x;
   const int kblk = L % nkb;
   const int grp = L / nkb;
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
 
-  const int key = kblk * kDkvKeysPerBlock + wave * 32 + l32;  // chunk index
+  const int key = kblk * KB + kw * 32 + l32;  // chunk index
   const bool key_ok = key < C;
   bf16x8 kreg[NKS], vreg[NKS];
   {
@@ -332,82 +372,125 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
 
-  // Query rows whose token is >= the block's first key can see some key of it.
-  const int r_begin = kblk * kDkvKeysPerBlock * G;
-  const bool stages_q = tid < NT;
-  const bool stages_g = tid >= 128 && tid < 128 + NT;
-  const int task = stages_q ? tid : tid - 128;
-  const int rg = task / CH, dg = task % CH;
+  // Rows whose token is >= the block's first key can see some key of it.
+  const int r_begin = kblk * KB * G;
+  const int n_steps = (rows - r_begin + BQ - 1) / BQ;
+  const bool stager = tid < NT;
+  const int tr0 = (tid / CH) * 4, td0 = (tid % CH) * 8;
 
-  for (int r0 = r_begin; r0 < rows; r0 += BQ) {
-    __syncthreads();
-    if (stages_q || stages_g) {
-      const uint16_t* src = stages_q ? p.q : p.d_o;
-      u32x4 w[4];
+  u32x4 rq[4], rg[4];
+  float pl = 0.f, pd = 0.f;
+  int ptok = -1;
+  auto issue = [&](int step) {
+    const int r0 = r_begin + step * BQ;
+    if (stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = r0 + rg * 4 + i;
+        const int rr = r0 + tr0 + i;
         if (rr < rows) {
           const int tt = rr / G;
-          const int hh = kv * G + (rr - tt * G);
-          const int64_t row = ((int64_t)b * p.Hq + hh) * C + tt;
-          w[i] = *reinterpret_cast<const u32x4*>(src + row * D + dg * 8);
+          const int64_t row = ((int64_t)b * p.Hq + kv * G + (rr - tt * G)) * C + tt;
+          rq[i] = *reinterpret_cast<const u32x4*>(p.q + row * D + td0);
+          rg[i] = *reinterpret_cast<const u32x4*>(p.d_o + row * D + td0);
         } else {
-          w[i] = u32x4{0u, 0u, 0u, 0u};
+          rq[i] = u32x4{0u, 0u, 0u, 0u};
+          rg[i] = u32x4{0u, 0u, 0u, 0u};
         }
       }
-      uint16_t* rowmajor = stages_q ? sm.q : sm.g;
-      uint16_t* trans = stages_q ? sm.qt : sm.gt;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x4*>(&rowmajor[(rg * 4 + i) * QS + dg * 8]) = w[i];
-      store_transposed(trans, QT, dg * 8, swap23(rg * 4), w);
     }
     if (tid < BQ) {
       const int rr = r0 + tid;
       if (rr < rows) {
         const int tt = rr / G;
-        const int hh = kv * G + (rr - tt * G);
-        const int64_t row = ((int64_t)b * p.Hq + hh) * C + tt;
-        sm.lse2[tid] = p.lse[row] * kLog2e;
-        sm.dlt[tid] = p.delta[row];
-        sm.tok[tid] = tt;
+        const int64_t row = ((int64_t)b * p.Hq + kv * G + (rr - tt * G)) * C + tt;
+        pl = p.lse[row] * kLog2e;
+        pd = p.delta[row];
+        ptok = tt;
       } else {
-        sm.lse2[tid] = 0.f;
-        sm.dlt[tid] = 0.f;
-        sm.tok[tid] = -1;
+        pl = 0.f;
+        pd = 0.f;
+        ptok = -1;
       }
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+    if (stager) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        *reinterpret_cast<u32x4*>(&sm.u.t.q[buf][prow(tr0 + i) * S + td0]) = rq[i];
+        *reinterpret_cast<u32x4*>(&sm.u.t.g[buf][prow(tr0 + i) * S + td0]) = rg[i];
+      }
+    }
+    if (tid < BQ) {
+      sm.lse2[buf][tid] = pl;
+      sm.dlt[buf][tid] = pd;
+      sm.tok[buf][tid] = ptok;
+    }
+  };
 
+  const int a_off = prow(l32) * S + hf * 8 + qb * 32 * S;  // this wave's 32 query rows
+  const int t_off = tr_lane_offset<S>(lane);
+
+  if (n_steps > 0) {
+    issue(0);
+    stage(0);
+    if (n_steps > 1) issue(1);
+    __syncthreads();
+  }
+  for (int step = 0; step < n_steps; ++step) {
+    const int cur = step & 1;
+    const uint16_t* qt = sm.u.t.q[cur];
+    const uint16_t* gt = sm.u.t.g[cur];
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      const int off = l32 * QS + ks * 16 + hf * 8;
-      s = mfma32(*reinterpret_cast<const bf16x8*>(&sm.q[off]), kreg[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(&sm.g[off]), vreg[ks], dp);
+      s = mfma32(*reinterpret_cast<const bf16x8*>(&qt[a_off + ks * 16]), kreg[ks], s);
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(&gt[a_off + ks * 16]), vreg[ks], dp);
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int qi = (i >> 2) * 8 + hf * 4 + (i & 3);
-      const float pv = (key <= sm.tok[qi])
-                           ? __builtin_amdgcn_exp2f(fmaf(s[i], c, -sm.lse2[qi]))
+      const int qi = qb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
+      const float pv = (key <= sm.tok[cur][qi])
+                           ? __builtin_amdgcn_exp2f(fmaf(s[i], c, -sm.lse2[cur][qi]))
                            : 0.f;
       pb[i >> 3][i & 7] = (__bf16)pv;
-      dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - sm.dlt[qi]));
+      dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - sm.dlt[cur][qi]));
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int ss = 0; ss < 2; ++ss) {
-        const int off = (db * 32 + l32) * QT + ss * 16 + hf * 8;
-        accv[db] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.gt[off]), pb[ss], accv[db]);
-        acck[db] = mfma32(*reinterpret_cast<const bf16x8*>(&sm.qt[off]), dsb[ss], acck[db]);
+        accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, qb * 32 + ss * 16, db * 32), pb[ss], accv[db]);
+        acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, qb * 32 + ss * 16, db * 32), dsb[ss], acck[db]);
       }
+    if (step + 1 < n_steps) {
+      stage(cur ^ 1);
+      if (step + 2 < n_steps) issue(step + 2);
+    }
+    __syncthreads();
   }
 
-  if (!key_ok) return;
+  // Waves 2-3 hand their partial sums to waves 0-1 through LDS (fp32, fixed order).
+  float* red = sm.u.red[kw];
+  if (qb == 1) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[(db * 16 + i) * 64 + lane] = acck[db][i];
+        red[32 * D + (db * 16 + i) * 64 + lane] = accv[db][i];
+      }
+  }
+  __syncthreads();
+  if (qb == 1 || !key_ok) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acck[db][i] += red[(db * 16 + i) * 64 + lane];
+      accv[db][i] += red[32 * D + (db * 16 + i) * 64 + lane];
+    }
   const float sc = p.scale;
   uint16_t* dkp = p.dk + (bh * C + key) * D;
   uint16_t* dvp = p.dv + (bh * C + key) * D;
@@ -437,11 +520,11 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   prof_begin(PKA_KERNEL_BWD_DQ, s);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CT>), dim3(p.plan.nblk), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DQ, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  const int nkb = (int)((p.C + kDkvKeysPerBlock - 1) / kDkvKeysPerBlock);
+  const int nkb = (int)((p.C + KB - 1) / KB);
   prof_begin(PKA_KERNEL_BWD_DKDV, s);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(p.B * p.Hkv * nkb), dim3(256), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DKDV, s);

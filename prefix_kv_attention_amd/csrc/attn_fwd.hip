@@ -7,19 +7,25 @@
 // reads the cached prefix as constants).
 //
 // Design (MI355X):
-//  * GQA packing: one workgroup serves 128 packed rows of one (window, KV head);
-//    packed row r is token r / G of query head kv*G + r % G, so all query heads
-//    that share a KV head read each staged K/V tile from LDS.
+//  * GQA packing: one workgroup of 8 waves serves 256 packed rows of one (window,
+//    KV head); packed row r is token r / G of query head kv*G + r % G, so every
+//    query head that shares a KV head reads each staged K/V tile from LDS.
 //  * Each wave owns 32 rows. Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16, so lane l holds all scores of query row l % 32 for
-//    16 keys: the online-softmax row max / row sum need one cross-lane exchange
-//    (lane l <-> l^32) per tile, and the running max, sum and rescale factor are
-//    per-lane scalars.
-//  * O^T += V^T P^T reuses the S^T registers (converted to bf16) directly as the
-//    MFMA B operand; V^T is staged in LDS with the matching key permutation.
-//  * The key sequence [cache rows ; chunk rows] is streamed in 64-key tiles;
-//    F16 / q8_0 cache rows are converted to bf16 while staging to LDS (dequantised
-//    on load). Only tiles that cross the causal diagonal are masked.
+//    v_mfma_f32_32x32x16_bf16, so lane l holds the scores of query row l % 32: the
+//    row max / row sum need one exchange (lane l <-> l^32) per tile, and the running
+//    max, sum and rescale factor are per-lane scalars.
+//  * O^T += V^T P^T: the S^T registers (converted to bf16) are the B operand as is;
+//    the V^T operand is read from the row-major V tile with the transposing LDS
+//    read, so no transposed copy is ever staged.
+//  * The key sequence [cache rows ; chunk rows] is streamed in 64-key tiles through
+//    two LDS buffers (one barrier per tile). Tiles that lie wholly in the cache use
+//    a fast path (uniform base pointer, fixed per-thread offsets); F16 / q8_0 rows
+//    are converted to bf16 while staging (dequantised on load). Only tiles that
+//    cross the causal diagonal are masked.
+//  * The running max is raised only when a row's tile max exceeds it by more than
+//    8 (in log2 units), so the rescale of the accumulator is skipped on almost every
+//    tile; probabilities then stay below 2^8, which bf16 and fp32 hold exactly
+//    enough. The result is the same softmax (any reference max gives it).
 //  * When (window, KV head, row block) units are too few to fill 256 CUs, the key
 //    tiles are split over several workgroups; partial (O, LSE) are merged by
 //    fwd_combine in a fixed order (deterministic).
@@ -30,58 +36,107 @@
 namespace pka {
 namespace {
 
-constexpr int BN = kKeysPerTile;
+constexpr int BN = kKeysPerTile;   // keys per tile
+constexpr int NW = kWavesPerBlock; // waves per workgroup
+constexpr int NTHR = 64 * NW;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 template <int D>
-struct FwdSmem {
-  static constexpr int KS = D + 8;   // row stride of K (bf16 elements)
-  static constexpr int VT = BN + 8;  // row stride of V^T
-  uint16_t k[BN * KS];
-  uint16_t vt[D * VT];
+struct FwdLds {
+  static constexpr int S = D + 8;
+  uint16_t k[2][BN * S];
+  uint16_t v[2][BN * S];
 };
 
-__device__ __forceinline__ uint32_t elem16(const u32x4& w, int e) {
-  return (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+// Raw rows of one staging task: 4 key rows x 8 values, as loaded from HBM.
+struct Task4 {
+  u32x4 w[4];
+  bool cache[4];
+};
+
+// Load task rows j0 .. j0+3 (8 values from column d0) of a tile lying wholly in the
+// cache: `base` points at row 0 of the tile.
+template <int CT, int D>
+__device__ __forceinline__ void load_fast(Task4& t, const char* base, const char* sbase,
+                                          int r0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (CT == kQ8) {
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base + (r0 + i) * D + d0);
+      const uint32_t s =
+          *reinterpret_cast<const uint16_t*>(sbase + ((r0 + i) * (D / 32) + (d0 >> 5)) * 2);
+      t.w[i] = u32x4{c.x, c.y, s, 0u};
+    } else {
+      t.w[i] = *reinterpret_cast<const u32x4*>(base + ((r0 + i) * D + d0) * 2);
+    }
+    t.cache[i] = true;
+  }
+}
+
+template <int CT, int D>
+__device__ __forceinline__ void load_general(Task4& t, const void* cache_base,
+                                             const uint16_t* cache_scale,
+                                             const uint16_t* chunk_base, int64_t P, int64_t C,
+                                             int64_t j0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    RawRow8 r;
+    t.cache[i] = load_row8<CT, D>(r, cache_base, cache_scale, chunk_base, P, C, j0 + i, d0);
+    t.w[i] = r.w;
+  }
+}
+
+template <int CT, int S>
+__device__ __forceinline__ void store_rows(uint16_t* tile, const Task4& t, int r0, int d0) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    RawRow8 r;
+    r.w = t.w[i];
+    *reinterpret_cast<u32x4*>(&tile[prow(r0 + i) * S + d0]) = to_bf16x8<CT>(r, t.cache[i]);
+  }
 }
 
 template <int D, int CT>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
-  __shared__ FwdSmem<D> sm;
-  constexpr int KS = FwdSmem<D>::KS;
-  constexpr int VT = FwdSmem<D>::VT;
-  constexpr int NKS = D / 16;           // k-steps over head_dim
-  constexpr int NDB = D / 32;           // 32-row blocks of O^T
-  constexpr int CH = D / 8;             // 8-value chunks per row
-  constexpr int NTASK = (BN / 4) * CH;  // staging tasks: 4 keys x 8 values
+__global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
+  __shared__ __align__(16) FwdLds<D> sm;
+  constexpr int S = FwdLds<D>::S;
+  constexpr int NKS = D / 16;   // k-steps over head_dim
+  constexpr int NDB = D / 32;   // 32-row blocks of O^T
+  constexpr int CH = D / 8;     // 8-value chunks per row
+  constexpr int NT = 16 * CH;   // staging tasks per tensor (4 rows x 8 values each)
+  constexpr int ESZ = (CT == kQ8) ? 1 : 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
 
-  const int n_rb = p.plan.n_rb, S = p.plan.n_split;
+  const int n_rb = p.plan.n_rb, SPL = p.plan.n_split;
   const int L = xcd_logical_id(blockIdx.x, p.plan.nblk);
   const int rb = L % n_rb;
-  const int split = (L / n_rb) % S;
-  const int grp = L / (n_rb * S);
+  const int split = (L / n_rb) % SPL;
+  const int grp = L / (n_rb * SPL);
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int G = p.G;
-  const int64_t C = p.C, P = p.P;
-  const int rows = G * (int)C;
+  const int C = (int)p.C;
+  const int P = (int)p.P;
+  const int rows = G * C;
+  constexpr int ROWS = 32 * NW;
 
-  const int r = rb * kRowsPerBlock + wave * 32 + l32;
+  const int r = rb * ROWS + wave * 32 + l32;
   const bool row_ok = r < rows;
   const int rr = row_ok ? r : rows - 1;
   const int t = rr / G;
   const int h = kv * G + (rr - t * G);
   const int64_t qrow = ((int64_t)b * p.Hq + h) * C + t;
 
-  const int r_first = rb * kRowsPerBlock;
-  const int r_last = min(rows - 1, r_first + kRowsPerBlock - 1);
+  const int r_first = rb * ROWS;
+  const int r_last = min(rows - 1, r_first + ROWS - 1);
   const int t_min = r_first / G, t_max = r_last / G;
-  const int64_t key_end = P + t_max + 1;
-  const int n_tiles = (int)((key_end + BN - 1) / BN);
-  const int tb = (int)((int64_t)split * n_tiles / S);
-  const int te = (int)((int64_t)(split + 1) * n_tiles / S);
+  const int key_end = P + t_max + 1;
+  const int n_tiles = (key_end + BN - 1) / BN;
+  const int tb = (int)((int64_t)split * n_tiles / SPL);
+  const int te = (int)((int64_t)(split + 1) * n_tiles / SPL);
+  const int n_fast = P / BN;  // tiles [0, n_fast) lie wholly in the cache
 
   bf16x8 qreg[NKS];
   {
@@ -91,65 +146,58 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
 
+  // Staging role: threads [0, NT) stage K, threads [256, 256 + NT) stage V.
+  const bool stage_k = tid < NT;
+  const bool stage_v = tid >= 256 && tid < 256 + NT;
+  const bool stager = stage_k || stage_v;
+  const int task = stage_k ? tid : tid - 256;
+  const int tr0 = (task / CH) * 4, td0 = (task % CH) * 8;  // task rows tr0..tr0+3, cols td0..
+
   const int64_t bh = (int64_t)b * p.Hkv + kv;
   const int64_t cap = p.cache.cap;
-  const void* ck;
-  const void* cv;
-  if constexpr (CT == kQ8) {
-    ck = static_cast<const int8_t*>(p.cache.k) + bh * cap * D;
-    cv = static_cast<const int8_t*>(p.cache.v) + bh * cap * D;
-  } else {
-    ck = static_cast<const uint16_t*>(p.cache.k) + bh * cap * D;
-    cv = static_cast<const uint16_t*>(p.cache.v) + bh * cap * D;
-  }
-  const uint16_t* cks = (CT == kQ8) ? p.cache.ks + bh * cap * (D / 32) : nullptr;
-  const uint16_t* cvs = (CT == kQ8) ? p.cache.vs + bh * cap * (D / 32) : nullptr;
-  const uint16_t* kcb = p.kc + bh * C * D;
-  const uint16_t* vcb = p.vc + bh * C * D;
+  const char* cbase = static_cast<const char*>(stage_k ? p.cache.k : p.cache.v) + bh * cap * D * ESZ;
+  const uint16_t* cscale = (CT == kQ8) ? (stage_k ? p.cache.ks : p.cache.vs) + bh * cap * (D / 32)
+                                       : nullptr;
+  const uint16_t* chunk = (stage_k ? p.kc : p.vc) + bh * (int64_t)C * D;
 
-  const bool has_task = tid < NTASK;
-  const int kg = tid / CH, dg = tid % CH;
-  RawRow8 rk[4], rv[4];
-  bool ik[4], iv[4];
-
+  Task4 raw;
   auto issue = [&](int tile) {
-    const int64_t j0 = (int64_t)tile * BN + kg * 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ik[i] = load_row8<CT, D>(rk[i], ck, cks, kcb, P, C, j0 + i, dg * 8);
-      iv[i] = load_row8<CT, D>(rv[i], cv, cvs, vcb, P, C, j0 + i, dg * 8);
+    if (tile < n_fast) {
+      load_fast<CT, D>(raw, cbase + (int64_t)tile * BN * D * ESZ,
+                       reinterpret_cast<const char*>(cscale + (int64_t)tile * BN * (D / 32)),
+                       tr0, td0);
+    } else {
+      load_general<CT, D>(raw, cbase, cscale, chunk, P, C, (int64_t)tile * BN + tr0, td0);
     }
   };
-  auto stage = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sm.k[(kg * 4 + i) * KS + dg * 8]) = to_bf16x8<CT>(rk[i], ik[i]);
-    u32x4 w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = to_bf16x8<CT>(rv[i], iv[i]);
-    const int pos = swap23(kg * 4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      u32x2 pr;
-      pr.x = elem16(w[0], e) | (elem16(w[1], e) << 16);
-      pr.y = elem16(w[2], e) | (elem16(w[3], e) << 16);
-      *reinterpret_cast<u32x2*>(&sm.vt[(dg * 8 + e) * VT + pos]) = pr;
-    }
+  auto stage = [&](int buf) {
+    store_rows<CT, S>(stage_k ? sm.k[buf] : sm.v[buf], raw, tr0, td0);
   };
+
+  // Per-lane LDS offsets of the MFMA operands.
+  const int k_off = prow(l32) * S + hf * 8;   // + kb*32*S + ks*16
+  const int v_off = tr_lane_offset<S>(lane);  // + (kb*32 + s*16)*S + db*32
 
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
   const float c = p.scale_log2;
-  const int64_t lim = P + t;  // this row may attend keys 0..lim
+  const float thr = kRescaleThreshold / c;  // raise the max only past m + thr
+  const int lim = P + t;                    // this row may attend keys 0..lim
 
-  if (tb < te && has_task) issue(tb);
+  if (tb < te) {
+    if (stager) {
+      issue(tb);
+      stage(0);
+      if (tb + 1 < te) issue(tb + 1);
+    }
+    __syncthreads();
+  }
   for (int tile = tb; tile < te; ++tile) {
-    __syncthreads();
-    if (has_task) stage();
-    __syncthreads();
-    if (tile + 1 < te && has_task) issue(tile + 1);
+    const int cur = (tile - tb) & 1;
+    const uint16_t* kt = sm.k[cur];
+    const uint16_t* vt = sm.v[cur];
 
     f32x16 st[2];
 #pragma unroll
@@ -157,20 +205,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       st[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&sm.k[(kb * 32 + l32) * KS + ks * 16 + hf * 8]);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
         st[kb] = mfma32(a, qreg[ks], st[kb]);
       }
     }
-    const int64_t kbase = (int64_t)tile * BN;
+    const int kbase = tile * BN;
     if (kbase + BN - 1 > P + t_min) {
+      const int rel = lim - kbase - hf * 4;  // key kbase + o + hf*4 allowed iff o <= rel
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int64_t key = kbase + kb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-          if (key > lim) st[kb][i] = -INFINITY;
-        }
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kb][i] = -INFINITY;
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -178,46 +224,51 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb][i]);
     mt = fmaxf(mt, wave_xor32(mt));
-    const float m_new = fmaxf(m, mt);
-    const float mc = (m_new == -INFINITY) ? 0.f : m_new * c;
-    const float alpha = __builtin_amdgcn_exp2f(m * c - mc);
+    const bool grow = mt > m + thr;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      // alpha = 1 for rows that keep their max; 0 for rows leaving -inf.
+      const float alpha = grow ? __builtin_amdgcn_exp2f((m - mt) * c) : 1.f;
+      const float m_new = grow ? mt : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m = m_new;
+    }
+    const float mc = (m == -INFINITY) ? 0.f : m * c;
     float ls = 0.f;
+    bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -mc));
-        st[kb][i] = pv;
         ls += pv;
+        pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
       }
-    l = l * alpha + ls;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kb * 2 + s][e] = (__bf16)st[kb][s * 8 + e];
+    l += ls;
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&sm.vt[(db * 32 + l32) * VT + kk * 16 + hf * 8]);
+        const bf16x8 a = lds_tr_operand<S>(vt, v_off, kk * 16, db * 32);
         acc[db] = mfma32(a, pb[kk], acc[db]);
       }
+
+    if (tile + 1 < te) {
+      if (stager) {
+        stage(cur ^ 1);
+        if (tile + 2 < te) issue(tile + 2);
+      }
+      __syncthreads();
+    }
   }
 
   const float l_tot = l + wave_xor32(l);
   if (!row_ok) return;
-  if (S == 1) {
+  if (SPL == 1) {
     const float inv = 1.f / l_tot;
     uint16_t* op = p.o + qrow * D;
 #pragma unroll
@@ -286,7 +337,7 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p) {
 template <int D, int CT>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   prof_begin(PKA_KERNEL_FWD, s);
-  hipLaunchKernelGGL((fwd_kernel<D, CT>), dim3(p.plan.nblk), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
   prof_end(PKA_KERNEL_FWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.plan.n_split == 1) return e;

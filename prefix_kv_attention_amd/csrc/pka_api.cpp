@@ -145,24 +145,25 @@ void prof_end(int kernel, hipStream_t s) {
   ++sl.used;
 }
 
-// One row block is 128 packed rows of one (window, KV head). When these units
-// cannot give every CU two workgroups, the key tiles are split; each split keeps
-// at least 8 tiles so the merge stays small next to the work.
+// One row block is kRowsPerBlock packed rows of one (window, KV head) and runs as
+// one 8-wave workgroup, one per CU. When these units are fewer than the CUs, the
+// key tiles are split so that units x splits still fits in one round of 256
+// workgroups; each split keeps at least 8 tiles so the merge stays small next to
+// the work.
 static Plan make_plan(const pka_dims& d) {
   Plan pl;
   const int64_t G = d.n_heads_q / d.n_heads_kv;
   pl.n_rb = (int)((G * d.chunk_len + kRowsPerBlock - 1) / kRowsPerBlock);
   const int64_t units = (int64_t)d.batch * d.n_heads_kv * pl.n_rb;
-  const int64_t target = 2 * kNumCUs;
-  int split = 1;
-  if (units < target) {
-    split = (int)((target + units - 1) / units);
+  int64_t split = 1;
+  if (units < kNumCUs) {
+    split = kNumCUs / units;
     const int64_t min_tiles = (d.prefix_len + 1 + kKeysPerTile - 1) / kKeysPerTile;
     const int64_t max_split = min_tiles / 8 > 1 ? min_tiles / 8 : 1;
-    if (split > max_split) split = (int)max_split;
+    if (split > max_split) split = max_split;
     if (split > 16) split = 16;
   }
-  pl.n_split = split;
+  pl.n_split = (int)split;
   pl.nblk = (int)(units * split);
   return pl;
 }

@@ -130,4 +130,51 @@ __device__ __forceinline__ float wave_xor32(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles. Every tile is row-major (one token row of D bf16 per row) with a
+// row stride of D + 8 elements, and the 8 rows of each aligned group are stored
+// in the order pi(r): r = 4a + b (a in {0,1}, b < 4) lands in physical row 2b + a.
+// With this layout, in a 32-bank LDS:
+//  * the 16-byte MFMA operand reads (lane -> one row, 8 consecutive values) of 8
+//    consecutive rows hit 8 distinct 4-bank groups, and
+//  * the transposing reads below (16 lanes -> a 4-row x 16-column block) hit 4
+//    distinct 8-bank groups,
+// while staging writes of whole rows by 16 consecutive lanes stay contiguous.
+__device__ __forceinline__ int prow(int r) {
+  return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+typedef v4i16 __attribute__((address_space(3))) * lds_v4i16_ptr;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane p receives element p%4
+// of the 8-byte pieces addressed by lanes p/4, p/4+4, p/4+8 and p/4+12. If lane q
+// of the group addresses row R0 + q/4, columns C0 + 4(q%4) .. +3 of a row-major
+// tile, lane p receives column C0 + p of rows R0 .. R0+3 (a 4x16 transpose).
+__device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16_ptr)((__attribute__((address_space(3))) uint16_t*)(p)));
+}
+
+// The transposed MFMA operand of one 32-row block: lane (l32, hf) of the wave
+// gets, for output row (column of the tile) C0 + l32 and k-step s of the 32
+// tile rows starting at R0, the 8 tile rows R0 + 16s + {0..3, 8..11} + 4 hf, in
+// the order that matches registers 8s..8s+7 of an MFMA result (see swap23).
+// `lane_base` is tr_lane_offset(lane); R0 must be a multiple of 32 (or 16 when
+// only s = 0 is used) and C0 a multiple of 32.
+template <int STRIDE>
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int q = lane & 15, hf = lane >> 5, h16 = (lane >> 4) & 1;
+  return prow(hf * 4 + (q >> 2)) * STRIDE + h16 * 16 + (q & 3) * 4;
+}
+template <int STRIDE>
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int lane_base,
+                                                 int r0, int c0) {
+  const v4i16 lo = lds_read_tr(tile + lane_base + r0 * STRIDE + c0);
+  const v4i16 hi = lds_read_tr(tile + lane_base + (r0 + 8) * STRIDE + c0);
+  const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 }  // namespace pka

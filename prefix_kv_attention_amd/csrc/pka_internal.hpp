@@ -9,9 +9,10 @@
 namespace pka {
 
 // Tile geometry shared by host planning and kernels.
-constexpr int kRowsPerBlock = 128;  // packed query rows per workgroup (4 waves x 32)
+constexpr int kWavesPerBlock = 8;   // waves per forward / dQ workgroup
+constexpr int kRowsPerBlock = 32 * kWavesPerBlock;  // packed query rows per workgroup
 constexpr int kKeysPerTile = 64;    // keys staged in LDS per step
-constexpr int kDkvKeysPerBlock = 128;  // chunk keys per dK/dV workgroup (4 waves x 32)
+constexpr int kDkvKeysPerBlock = 64;   // chunk keys per dK/dV workgroup (2 x 32)
 constexpr int kNumCUs = 256;        // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCDs = 8;
 
