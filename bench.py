@@ -195,7 +195,7 @@ def main():
     kernels = {}
     if kernel_events:
         for name in ("fwd", "fwd_combine", "bwd_prep", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce",
-                     "append"):
+                     "bwd_dkdv_reduce", "append"):
             tot, n, _ = pka.profile_read(name)
             if n:
                 kernels[name] = round(tot / n, 5)

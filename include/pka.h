@@ -170,7 +170,8 @@ typedef enum {
   PKA_KERNEL_BWD_DQ_REDUCE = 5, /* sum of dq split partials                        */
   PKA_KERNEL_APPEND = 6,     /* kv_append_*                                        */
   PKA_KERNEL_DEQUANT = 7,    /* kv_dequant_q8_0                                    */
-  PKA_KERNEL_COUNT = 8
+  PKA_KERNEL_BWD_DKDV_REDUCE = 8, /* sum of dk, dv row-split partials              */
+  PKA_KERNEL_COUNT = 9
 } pka_kernel_id;
 
 pka_status pka_profile_enable(int32_t on);

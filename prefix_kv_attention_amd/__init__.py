@@ -32,7 +32,7 @@ CACHE_TYPE_BY_NAME = {"f16": CACHE_F16, "bf16": CACHE_BF16, "q8_0": CACHE_Q8_0}
 STATUS = {0: "PKA_OK", 1: "PKA_ERR_NULL", 2: "PKA_ERR_DIMS", 3: "PKA_ERR_UNSUPPORTED",
           4: "PKA_ERR_CAPACITY", 5: "PKA_ERR_ALIGN", 6: "PKA_ERR_WORKSPACE", 7: "PKA_ERR_HIP"}
 KERNELS = {"fwd": 0, "fwd_combine": 1, "bwd_prep": 2, "bwd_dq": 3, "bwd_dkdv": 4,
-           "bwd_dq_reduce": 5, "append": 6, "dequant": 7}
+           "bwd_dq_reduce": 5, "append": 6, "dequant": 7, "bwd_dkdv_reduce": 8}
 
 
 class Dims(ctypes.Structure):

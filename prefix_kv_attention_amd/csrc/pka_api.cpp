@@ -165,11 +165,31 @@ static Plan make_plan(const pka_dims& d) {
   }
   pl.n_split = (int)split;
   pl.nblk = (int)(units * split);
+  pl.n_dkv_split = 1;
   return pl;
 }
 
 Plan plan_fwd(const pka_dims& d) { return make_plan(d); }
-Plan plan_bwd(const pka_dims& d) { return make_plan(d); }
+
+// dK/dV: one unit per (window, KV head, block of kDkvKeysPerBlock chunk keys). Few
+// units are split over disjoint ranges of query rows (each split keeps >= 2 steps
+// of 64 rows of the longest unit); their fp32 partials are summed afterwards.
+Plan plan_bwd(const pka_dims& d) {
+  Plan pl = make_plan(d);
+  const int64_t G = d.n_heads_q / d.n_heads_kv;
+  const int64_t nkb = (d.chunk_len + kDkvKeysPerBlock - 1) / kDkvKeysPerBlock;
+  const int64_t units = (int64_t)d.batch * d.n_heads_kv * nkb;
+  int64_t split = 1;
+  if (units < kNumCUs) {
+    split = kNumCUs / units;
+    const int64_t max_steps = (G * d.chunk_len + 63) / 64;
+    const int64_t max_split = max_steps / 2 > 1 ? max_steps / 2 : 1;
+    if (split > max_split) split = max_split;
+    if (split > 16) split = 16;
+  }
+  pl.n_dkv_split = (int)split;
+  return pl;
+}
 
 }  // namespace pka
 
@@ -208,6 +228,9 @@ size_t pka_bwd_workspace_bytes(const pka_dims* dims) {
   const size_t nrow = (size_t)dims->batch * dims->n_heads_q * dims->chunk_len;
   size_t bytes = align256(nrow * 4);  // delta
   if (pl.n_split > 1) bytes += align256((size_t)pl.n_split * nrow * dims->head_dim * 4);
+  if (pl.n_dkv_split > 1)
+    bytes += align256((size_t)pl.n_dkv_split * 2 * dims->batch * dims->n_heads_kv *
+                      dims->chunk_len * dims->head_dim * 4);
   return bytes;
 }
 
@@ -293,8 +316,12 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
   const size_t nrow = (size_t)p.B * p.Hq * p.C;
   float* ws_delta = static_cast<float*>(ws);
   p.delta = delta ? delta : ws_delta;
-  if (p.plan.n_split > 1)
-    p.ws_dq = reinterpret_cast<float*>(static_cast<char*>(ws) + align256(nrow * 4));
+  size_t off = align256(nrow * 4);
+  if (p.plan.n_split > 1) {
+    p.ws_dq = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
+    off += align256((size_t)p.plan.n_split * nrow * dims->head_dim * 4);
+  }
+  if (p.plan.n_dkv_split > 1) p.ws_dkv = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   hipError_t e = launch_bwd(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk_attn_bwd launch");
   return PKA_OK;

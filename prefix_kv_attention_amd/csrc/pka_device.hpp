@@ -132,16 +132,15 @@ __device__ __forceinline__ float wave_xor32(float v) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles. Every tile is row-major (one token row of D bf16 per row) with a
-// row stride of D + 8 elements, and the 8 rows of each aligned group are stored
-// in the order pi(r): r = 4a + b (a in {0,1}, b < 4) lands in physical row 2b + a.
-// With this layout, in a 32-bank LDS:
-//  * the 16-byte MFMA operand reads (lane -> one row, 8 consecutive values) of 8
-//    consecutive rows hit 8 distinct 4-bank groups, and
-//  * the transposing reads below (16 lanes -> a 4-row x 16-column block) hit 4
-//    distinct 8-bank groups,
-// while staging writes of whole rows by 16 consecutive lanes stay contiguous.
+// row stride of D + 8 elements, and the 16 rows of each aligned group are stored
+// in the order prow(r): r = 4a + b (a, b < 4) lands in physical row 4b + a.
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT of a probe of both access kinds), this
+// layout makes both the 16-byte MFMA operand reads (lane -> one row, 8
+// consecutive values) and the transposing reads below (16 lanes -> a 4-row x
+// 16-column block) conflict-free; staging writes of whole rows by 16 consecutive
+// lanes stay contiguous.
 __device__ __forceinline__ int prow(int r) {
-  return (r & ~7) | ((r & 3) << 1) | ((r >> 2) & 1);
+  return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -157,22 +156,25 @@ __device__ __forceinline__ v4i16 lds_read_tr(const uint16_t* p) {
       (lds_v4i16_ptr)((__attribute__((address_space(3))) uint16_t*)(p)));
 }
 
-// The transposed MFMA operand of one 32-row block: lane (l32, hf) of the wave
-// gets, for output row (column of the tile) C0 + l32 and k-step s of the 32
-// tile rows starting at R0, the 8 tile rows R0 + 16s + {0..3, 8..11} + 4 hf, in
-// the order that matches registers 8s..8s+7 of an MFMA result (see swap23).
-// `lane_base` is tr_lane_offset(lane); R0 must be a multiple of 32 (or 16 when
-// only s = 0 is used) and C0 a multiple of 32.
+// The transposed MFMA operand of one 16-row k-step: lane (l32, hf) of the wave
+// gets, for output row (column of the tile) C0 + l32, the 8 tile rows
+// R0 + {0..3, 8..11} + 4 hf, in the order that matches registers 8s..8s+7 of an
+// MFMA result (see swap23). R0 must be a multiple of 16 and C0 of 32.
+struct TrOffsets {
+  int lo, hi;  // per-lane element offsets of the two 4-row reads
+};
 template <int STRIDE>
-__device__ __forceinline__ int tr_lane_offset(int lane) {
+__device__ __forceinline__ TrOffsets tr_lane_offsets(int lane) {
   const int q = lane & 15, hf = lane >> 5, h16 = (lane >> 4) & 1;
-  return prow(hf * 4 + (q >> 2)) * STRIDE + h16 * 16 + (q & 3) * 4;
+  const int col = h16 * 16 + (q & 3) * 4;
+  const int y = hf * 4 + (q >> 2);
+  return TrOffsets{prow(y) * STRIDE + col, prow(8 + y) * STRIDE + col};
 }
 template <int STRIDE>
-__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, int lane_base,
+__device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, const TrOffsets& o,
                                                  int r0, int c0) {
-  const v4i16 lo = lds_read_tr(tile + lane_base + r0 * STRIDE + c0);
-  const v4i16 hi = lds_read_tr(tile + lane_base + (r0 + 8) * STRIDE + c0);
+  const v4i16 lo = lds_read_tr(tile + o.lo + r0 * STRIDE + c0);
+  const v4i16 hi = lds_read_tr(tile + o.hi + r0 * STRIDE + c0);
   const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }

@@ -27,9 +27,10 @@ struct CacheRef {
 
 // Work plan of the forward / dQ grids: units of (window, KV head, row block, split).
 struct Plan {
-  int n_rb;     // row blocks of 128 packed rows per (window, KV head)
+  int n_rb;     // row blocks of kRowsPerBlock packed rows per (window, KV head)
   int n_split;  // prefix splits per row block
   int nblk;     // workgroups = B * Hkv * n_rb * n_split
+  int n_dkv_split;  // backward only: query-row splits per dK/dV key block
 };
 
 struct FwdParams {
@@ -61,6 +62,7 @@ struct BwdParams {
   uint16_t* dv;
   float* delta;   // [B*Hq*C]: caller's buffer or workspace
   float* ws_dq;   // [n_split][B*Hq*C][D] (only when n_split > 1)
+  float* ws_dkv;  // [n_dkv_split][2][B*Hkv*C][D] (only when n_dkv_split > 1)
   int B, Hq, Hkv, G;
   int64_t P, C;
   float scale;
