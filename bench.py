@@ -53,6 +53,19 @@ def prefix_bytes(w):
     return 2 * rows * per_row   # K and V
 
 
+def source_digest(files):
+    """First 16 hex digits of the SHA-256 of the kernel sources a figure was taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "prefix_kv_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+TRAFFIC_SOURCES = ("attn_bwd.hip", "pka_device.hpp", "pka_internal.hpp")
+
+
 def read_traffic(kernel_name):
     """HBM bytes per launch from the committed counter summary, if still current."""
     path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.txt")
@@ -64,10 +77,8 @@ def read_traffic(kernel_name):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
     try:
-        import hashlib
-        src = open(os.path.join(ROOT, "prefix_kv_attention_amd", "csrc",
-                                vals["source_file"]), "rb").read()
-        if hashlib.sha256(src).hexdigest()[:16] != vals["source_sha256_16"]:
+        files = [f.strip() for f in vals["source_files"].split(",")]
+        if source_digest(files) != vals["source_sha256_16"]:
             return None
         return float(vals["bytes_per_launch"])
     except (KeyError, OSError, ValueError):
