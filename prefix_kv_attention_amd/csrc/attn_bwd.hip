@@ -326,9 +326,9 @@ struct DkvLds {
     } t;
     float red[2][32 * D * 2];  // partial dK^T, dV^T of waves 2-3 (fp32)
   } u;
-  float lse2[2][BQ];
-  float dlt[2][BQ];
-  int tok[2][BQ];
+  __align__(16) float lse2[2][BQ];
+  __align__(16) float dlt[2][BQ];
+  __align__(16) int tok[2][BQ];
 };
 
 template <int D>
@@ -392,39 +392,62 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const bool stager = tid < NT;
   const int tr0 = (tid / CH) * 4, td0 = (tid % CH) * 8;
 
+  // Packed row rr is token rr / G of query head kv*G + rr % G. Each thread follows
+  // its rows from step to step (+BQ rows per step) without dividing.
+  const int dt_step = BQ / G, dg_step = BQ % G;
+  const int64_t head0 = (int64_t)b * p.Hq + kv * G;   // first query head of this KV head
+  int tq[4], gq[4];       // (token, head-in-group) of the 4 staged rows
+  int tl = 0, gl = 0;     // same for the row whose LSE / delta this thread stages
+  {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rr = r_begin + tr0 + i;
+      tq[i] = rr / G;
+      gq[i] = rr - tq[i] * G;
+    }
+    const int rr = r_begin + tid;
+    tl = rr / G;
+    gl = rr - tl * G;
+  }
+  auto advance = [&](int& t, int& g) {
+    t += dt_step;
+    g += dg_step;
+    if (g >= G) {
+      g -= G;
+      t += 1;
+    }
+  };
   u32x4 rq[4], rg[4];
   float pl = 0.f, pd = 0.f;
   int ptok = -1;
-  auto issue = [&](int step) {
+  auto issue = [&](int step) {   // called for steps 0, 1, 2, ... in order
     const int r0 = r_begin + step * BQ;
     if (stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rr = r0 + tr0 + i;
-        if (rr < rows) {
-          const int tt = rr / G;
-          const int64_t row = ((int64_t)b * p.Hq + kv * G + (rr - tt * G)) * C + tt;
+        if (r0 + tr0 + i < rows) {
+          const int64_t row = (head0 + gq[i]) * C + tq[i];
           rq[i] = *reinterpret_cast<const u32x4*>(p.q + row * D + td0);
           rg[i] = *reinterpret_cast<const u32x4*>(p.d_o + row * D + td0);
         } else {
           rq[i] = u32x4{0u, 0u, 0u, 0u};
           rg[i] = u32x4{0u, 0u, 0u, 0u};
         }
+        advance(tq[i], gq[i]);
       }
     }
     if (tid < BQ) {
-      const int rr = r0 + tid;
-      if (rr < rows) {
-        const int tt = rr / G;
-        const int64_t row = ((int64_t)b * p.Hq + kv * G + (rr - tt * G)) * C + tt;
+      if (r0 + tid < rows) {
+        const int64_t row = (head0 + gl) * C + tl;
         pl = p.lse[row] * kLog2e;
         pd = p.delta[row];
-        ptok = tt;
+        ptok = tl;
       } else {
         pl = 0.f;
         pd = 0.f;
         ptok = -1;
       }
+      advance(tl, gl);
     }
   };
   auto stage = [&](int buf) {
@@ -463,13 +486,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
     bf16x8 pb[2], dsb[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int qi = qb * 32 + (i >> 2) * 8 + hf * 4 + (i & 3);
-      const float pv = (key <= sm.tok[cur][qi])
-                           ? __builtin_amdgcn_exp2f(fmaf(s[i], c, -sm.lse2[cur][qi]))
-                           : 0.f;
-      pb[i >> 3][i & 7] = (__bf16)pv;
-      dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - sm.dlt[cur][qi]));
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // result rows (g4*8 + hf*4 + 0..3) of this wave's 32 query rows: one 16-byte
+      // read per per-row array
+      const int q0 = qb * 32 + g4 * 8 + hf * 4;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][q0]);
+      const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
+      const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = g4 * 4 + j;
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l4[j]));
+        const float pv = key <= tk[j] ? e : 0.f;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - d4[j]));
+      }
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
