@@ -8,8 +8,9 @@
 // an attention backward that computes gradient for the kept queries only).
 //
 // Kernels, in launch order on the caller's stream:
-//  1. bwd_prep:  delta_i = sum_d dO_id * O_id from the stored bf16 O.
-//  2. bwd_dq:    per 256 packed query rows (GQA packing as in the forward), stream
+//  1. bwd_dq:    delta_i = sum_d dO_id * O_id from the stored bf16 O (prologue; the
+//                first split of each row writes it for bwd_dkdv), then per 256
+//                packed query rows (GQA packing as in the forward), stream
 //                the key tiles: S^T = K Q^T and dP^T = V dO^T (MFMA bf16),
 //                P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - delta) in
 //                registers, dQ^T += K^T dS^T with the dS^T registers as the B operand
@@ -17,7 +18,7 @@
 //                Split over key tiles like the forward when the units are too few;
 //                fp32 partials are summed by bwd_dq_reduce in a fixed order. MFMA
 //                blocks run at raised wave priority (measured ~1.5% faster).
-//  3. bwd_dkdv:  per 64 chunk keys of one (window, KV head), stream the packed
+//  2. bwd_dkdv:  per 64 chunk keys of one (window, KV head), stream the packed
 //                query rows of all G heads that can see them (token >= key) in tiles
 //                of 64: S = Q K^T and dP = dO V^T with keys as MFMA columns, then
 //                dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposing reads).
@@ -36,30 +37,6 @@ namespace {
 constexpr int BN = kKeysPerTile;
 constexpr int NW = kWavesPerBlock;
 constexpr int NTHR = 64 * NW;
-
-__device__ __forceinline__ uint32_t elem16(const u32x4& w, int e) {
-  return (w[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
-  constexpr int CH = D / 8;
-  const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = idx / CH;
-  const int c8 = (int)(idx % CH);
-  float s = 0.f;
-  if (row < nrow) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(p.o + row * D + c8 * 8);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(p.d_o + row * D + c8 * 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      s = fmaf(bf16_to_f32(elem16(a, e)), bf16_to_f32(elem16(g, e)), s);
-  }
-#pragma unroll
-  for (int off = CH / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-  if (row < nrow && c8 == 0) p.delta[row] = s;
-}
 
 // Raw rows of one staging task: 4 rows x 8 values, as loaded from HBM.
 struct Task4 {
@@ -168,8 +145,6 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
   const float lse2 = p.lse[qrow] * kLog2e;
-  const float dlt = p.delta[qrow];
-
   const bool stage_k = tid < NT;
   const bool stage_v = tid >= 256 && tid < 256 + NT;
   const bool stager = stage_k || stage_v;
@@ -205,9 +180,25 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   const int lim = P + t;
 
+  if (tb < te && stager) issue(tb);
+  // delta = rowsum(dO * O) of this lane's row: each lane-half holds half of the dO
+  // row (the B-operand layout), so read the same half of O and add the halves.
+  float dlt;  // computed while the first tile is in flight
+  {
+    const uint16_t* op = p.o + qrow * D + hf * 8;
+    float sdot = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const bf16x8 ov = *reinterpret_cast<const bf16x8*>(op + ks * 16);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sdot = fmaf((float)ov[e], (float)oreg[ks][e], sdot);
+    }
+    dlt = sdot + wave_xor32(sdot);
+    if (split == 0 && row_ok && hf == 0) p.delta[qrow] = dlt;  // read by bwd_dkdv
+  }
+
   if (tb < te) {
     if (stager) {
-      issue(tb);
       stage(0);
       if (tb + 1 < te) issue(tb + 1);
     }
@@ -605,12 +596,7 @@ template <int D, int CT>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
   const unsigned row_blocks = (unsigned)((nrow * (D / 8) + 255) / 256);
-  prof_begin(PKA_KERNEL_BWD_PREP, s);
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3(row_blocks), dim3(256), 0, s, p);
-  prof_end(PKA_KERNEL_BWD_PREP, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
+  hipError_t e;
   prof_begin(PKA_KERNEL_BWD_DQ, s);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DQ, s);

@@ -101,14 +101,20 @@ __device__ __forceinline__ u32x4 to_bf16x8(const RawRow8& r, bool is_cache) {
     }
     return o;
   } else {
+    // d * q exactly: with u = q + 128 in [1, 255] (flip the sign bit of each byte),
+    // d*u is exact in fp32 (11 + 8 significant bits) and fma(d, u, -128 d) rounds
+    // the exact d*q once, which is representable -- so this equals fl32(d * q) while
+    // each value costs one unsigned-byte conversion and one fma.
     const float d = f16_to_f32(r.w.z);
+    const float nd = -128.f * d;
+    const uint32_t x = r.w.x ^ 0x80808080u, y = r.w.y ^ 0x80808080u;
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t w = (i < 2) ? r.w.x : r.w.y;
+      const uint32_t w = (i < 2) ? x : y;
       const int sh = (i & 1) * 16;
-      const float a = d * (float)(int8_t)((w >> sh) & 0xff);
-      const float b = d * (float)(int8_t)((w >> (sh + 8)) & 0xff);
+      const float a = fmaf(d, (float)((w >> sh) & 0xffu), nd);
+      const float b = fmaf(d, (float)((w >> (sh + 8)) & 0xffu), nd);
       o[i] = pack_bf16(a, b);
     }
     return o;
