@@ -167,10 +167,10 @@ typedef enum {
   PKA_KERNEL_BWD_PREP = 2,   /* reserved: delta is now computed inside bwd_dq      */
   PKA_KERNEL_BWD_DQ = 3,     /* dq over prefix and chunk keys                      */
   PKA_KERNEL_BWD_DKDV = 4,   /* chunk-only dk, dv                                  */
-  PKA_KERNEL_BWD_DQ_REDUCE = 5, /* sum of dq split partials                        */
+  PKA_KERNEL_BWD_DQ_REDUCE = 5, /* sums of dq and dk/dv split partials (one launch) */
   PKA_KERNEL_APPEND = 6,     /* kv_append_*                                        */
   PKA_KERNEL_DEQUANT = 7,    /* kv_dequant_q8_0                                    */
-  PKA_KERNEL_BWD_DKDV_REDUCE = 8, /* sum of dk, dv row-split partials              */
+  PKA_KERNEL_BWD_DKDV_REDUCE = 8, /* reserved: folded into PKA_KERNEL_BWD_DQ_REDUCE */
   PKA_KERNEL_COUNT = 9
 } pka_kernel_id;
 

@@ -16,7 +16,7 @@
 //                registers, dQ^T += K^T dS^T with the dS^T registers as the B operand
 //                and K^T read from the row-major K tile by the transposing LDS read.
 //                Split over key tiles like the forward when the units are too few;
-//                fp32 partials are summed by bwd_dq_reduce in a fixed order. MFMA
+//                fp32 partials are summed by bwd_reduce in a fixed order. MFMA
 //                blocks run at raised wave priority (measured ~1.5% faster).
 //  2. bwd_dkdv:  per 64 chunk keys of one (window, KV head), stream the packed
 //                query rows of all G heads that can see them (token >= key) in tiles
@@ -27,7 +27,7 @@
 //                The sum over the G heads of a KV head falls out of the packing.
 //                When (window, KV head, key block) units are few, each is split
 //                over disjoint query-row ranges whose fp32 partials
-//                bwd_dkdv_reduce sums in a fixed order.
+//                bwd_reduce sums in a fixed order (one launch with the dQ sums).
 // No atomics anywhere: every output element is owned by one lane (deterministic).
 #include "pka_device.hpp"
 
@@ -280,29 +280,6 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dq_reduce_kernel(BwdParams p) {
-  constexpr int CH = D / 8;
-  const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = idx / CH;
-  const int c8 = (int)(idx % CH);
-  if (row >= nrow) return;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.plan.n_split; ++s) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(p.ws_dq + (s * nrow + row) * D + c8 * 8);
-    const f32x4 a = src[0], bq = src[1];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[i] += a[i];
-      o[4 + i] += bq[i];
-    }
-  }
-  u32x4 out = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-               pack_bf16(o[6], o[7])};
-  *reinterpret_cast<u32x4*>(p.dq + row * D + c8 * 8) = out;
-}
-
 // ------------------------------------------------------------------ dK / dV
 constexpr int BQ = 64;                      // packed query rows per step
 constexpr int KB = kDkvKeysPerBlock;        // chunk keys per workgroup (64)
@@ -530,7 +507,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
   const float sc = p.scale;
   if (RS > 1) {
-    // fp32 partials of this row split, summed in split order by bwd_dkdv_reduce.
+    // fp32 partials of this row split, summed in split order by bwd_reduce.
     const int64_t nkey = (int64_t)p.B * p.Hkv * C;
     float* pk = p.ws_dkv + ((int64_t)rsplit * 2 * nkey + bh * C + key) * D;
     float* pv = pk + nkey * D;
@@ -565,37 +542,56 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
     }
 }
 
-// Sum of the dK/dV row-split partials (fixed split order), written as bf16.
+// Sums of split partials, in split order, written as bf16 (one launch for both):
+// threads [0, n_dq) reduce dQ rows (prefix split of the dQ kernel), the rest reduce
+// dK and dV rows (query-row split of the dK/dV kernel).
 template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_reduce_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_dq,
+                                                         int64_t n_dkv) {
   constexpr int CH = D / 8;
-  const int64_t nkey = (int64_t)p.B * p.Hkv * p.C;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 2 * nkey * CH) return;
-  const int which = (int)(idx / (nkey * CH));   // 0: dK, 1: dV
-  const int64_t rem = idx - which * nkey * CH;
-  const int64_t row = rem / CH;
-  const int c8 = (int)(rem % CH);
+  int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const float* src;
+  int64_t stride;  // floats between consecutive splits
+  int nsplit;
+  uint16_t* dst;
+  if (idx < n_dq) {
+    const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
+    const int64_t row = idx / CH;
+    const int c8 = (int)(idx % CH);
+    src = p.ws_dq + row * D + c8 * 8;
+    stride = nrow * D;
+    nsplit = p.plan.n_split;
+    dst = p.dq + row * D + c8 * 8;
+  } else {
+    idx -= n_dq;
+    if (idx >= n_dkv) return;   // n_dkv is 0 when dK/dV rows were not split
+    const int64_t nkey = (int64_t)p.B * p.Hkv * p.C;
+    const int which = (int)(idx / (nkey * CH));   // 0: dK, 1: dV
+    const int64_t rem = idx - which * nkey * CH;
+    const int64_t row = rem / CH;
+    const int c8 = (int)(rem % CH);
+    src = p.ws_dkv + (which * nkey + row) * D + c8 * 8;
+    stride = 2 * nkey * D;
+    nsplit = p.plan.n_dkv_split;
+    dst = (which ? p.dv : p.dk) + row * D + c8 * 8;
+  }
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < p.plan.n_dkv_split; ++s) {
-    const f32x4* src = reinterpret_cast<const f32x4*>(
-        p.ws_dkv + (((int64_t)s * 2 + which) * nkey + row) * D + c8 * 8);
-    const f32x4 a = src[0], bq = src[1];
+  for (int s = 0; s < nsplit; ++s) {
+    const f32x4* v = reinterpret_cast<const f32x4*>(src + (int64_t)s * stride);
+    const f32x4 a = v[0], bq = v[1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       o[i] += a[i];
       o[4 + i] += bq[i];
     }
   }
-  u32x4 out = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
-               pack_bf16(o[6], o[7])};
-  *reinterpret_cast<u32x4*>((which ? p.dv : p.dk) + row * D + c8 * 8) = out;
+  *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
+                                         pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
 }
 
 template <int D, int CT>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
-  const unsigned row_blocks = (unsigned)((nrow * (D / 8) + 255) / 256);
   hipError_t e;
   prof_begin(PKA_KERNEL_BWD_DQ, s);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
@@ -608,18 +604,13 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
                      dim3(256), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DKDV, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.plan.n_dkv_split > 1) {
-    const int64_t threads = 2 * (int64_t)p.B * p.Hkv * p.C * (D / 8);
-    prof_begin(PKA_KERNEL_BWD_DKDV_REDUCE, s);
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)((threads + 255) / 256)),
-                       dim3(256), 0, s, p);
-    prof_end(PKA_KERNEL_BWD_DKDV_REDUCE, s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
 
-  if (p.plan.n_split > 1) {
+  const int64_t n_dq = p.plan.n_split > 1 ? nrow * (D / 8) : 0;
+  const int64_t n_dkv = p.plan.n_dkv_split > 1 ? 2 * (int64_t)p.B * p.Hkv * p.C * (D / 8) : 0;
+  if (n_dq + n_dkv > 0) {
     prof_begin(PKA_KERNEL_BWD_DQ_REDUCE, s);
-    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>), dim3(row_blocks), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n_dq + n_dkv + 255) / 256)),
+                       dim3(256), 0, s, p, n_dq, n_dkv);
     prof_end(PKA_KERNEL_BWD_DQ_REDUCE, s);
     e = hipGetLastError();
   }

@@ -47,6 +47,15 @@ EDGE = [
     synthetic.small("g6-c512", batch=1, prefix_len=1500, chunk_len=512, n_heads_q=6,
                     n_heads_kv=1, head_dim=128, cache_type="q8_0", qkv_std=0.1,
                     prefix_std=1.0, do_std=1e-2, outlier_frac=0.01),
+    # prefix split of dQ without a row split of dK/dV (64 dQ units, 256 dK/dV units)
+    synthetic.small("dq-split-only", batch=2, prefix_len=2048, chunk_len=1024, n_heads_q=8,
+                    n_heads_kv=8, head_dim=64, cache_type="bf16", qkv_std=0.3, prefix_std=0.3),
+    # row split of dK/dV without a prefix split of dQ (256 dQ units, 64 dK/dV units)
+    synthetic.small("dkv-split-only", batch=8, prefix_len=128, chunk_len=64, n_heads_q=128,
+                    n_heads_kv=8, head_dim=64, cache_type="f16", qkv_std=0.3, prefix_std=0.3),
+    # plain causal attention over a long chunk: every tile crosses the chunk
+    synthetic.small("p0-c2048", batch=1, prefix_len=0, chunk_len=2048, n_heads_q=4,
+                    n_heads_kv=2, head_dim=128, cache_type="bf16", qkv_std=0.3),
 ]
 
 
@@ -276,3 +285,34 @@ def test_error_paths_raise_before_launch():
     q96 = torch.zeros((1, 2, 16, 96), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(pka.PkaError, match="UNSUPPORTED"):
         pka.chunk_attn_fwd(q96, q96[:, :1], q96[:, :1], case.cache, 64, 0.1)
+
+
+@pytest.mark.parametrize("ct", ["q8_0", "f16", "bf16"])
+def test_forward_backward_leave_cache_untouched(ct):
+    """The prefix is read-only and stop-gradient: fwd and bwd change no cache byte."""
+    w = synthetic.small(f"ro-{ct}", batch=2, prefix_len=640, chunk_len=96, n_heads_q=4,
+                        n_heads_kv=2, head_dim=128, cache_type=ct, prefix_std=1.0)
+    case = Case(w, extra_capacity=32)
+    before = [t.clone() for t in (case.cache.k, case.cache.v, case.cache.k_scale,
+                                  case.cache.v_scale) if t is not None]
+    o, lse = case.fwd()
+    case.bwd(o, lse)
+    torch.cuda.synchronize()
+    after = [t for t in (case.cache.k, case.cache.v, case.cache.k_scale, case.cache.v_scale)
+             if t is not None]
+    for a, b in zip(before, after):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_parity_group1_full_width():
+    """G = 1 (no GQA) at the headline's P and C, sampled groups."""
+    w = synthetic.HEADLINE.with_(name="g1-16k", batch=2, n_heads_q=8, n_heads_kv=8, seed=9)
+    print(_label(w), flush=True)
+    case = Case(w)
+    o, lse = case.fwd()
+    dq, dk, dv = case.bwd(o, lse)
+    torch.cuda.synchronize()
+    groups = case.all_groups()
+    errs = compare_groups(case, [groups[0], groups[-1]], o, lse, dq, dk, dv)
+    print(errs, flush=True)
+    assert_within(errs, _label(w))
