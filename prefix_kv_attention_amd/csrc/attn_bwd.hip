@@ -38,52 +38,6 @@ constexpr int BN = kKeysPerTile;
 constexpr int NW = kWavesPerBlock;
 constexpr int NTHR = 64 * NW;
 
-// Raw rows of one staging task: 4 rows x 8 values, as loaded from HBM.
-struct Task4 {
-  u32x4 w[4];
-  bool cache[4];
-};
-
-template <int CT, int D>
-__device__ __forceinline__ void load_fast(Task4& t, const char* base, const char* sbase,
-                                          int r0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (CT == kQ8) {
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + (r0 + i) * D + d0);
-      const uint32_t s =
-          *reinterpret_cast<const uint16_t*>(sbase + ((r0 + i) * (D / 32) + (d0 >> 5)) * 2);
-      t.w[i] = u32x4{c.x, c.y, s, 0u};
-    } else {
-      t.w[i] = *reinterpret_cast<const u32x4*>(base + ((r0 + i) * D + d0) * 2);
-    }
-    t.cache[i] = true;
-  }
-}
-
-template <int CT, int D>
-__device__ __forceinline__ void load_general(Task4& t, const void* cache_base,
-                                             const uint16_t* cache_scale,
-                                             const uint16_t* chunk_base, int64_t P, int64_t C,
-                                             int64_t j0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    RawRow8 r;
-    t.cache[i] = load_row8<CT, D>(r, cache_base, cache_scale, chunk_base, P, C, j0 + i, d0);
-    t.w[i] = r.w;
-  }
-}
-
-template <int CT, int S>
-__device__ __forceinline__ void store_rows(uint16_t* tile, const Task4& t, int r0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    RawRow8 r;
-    r.w = t.w[i];
-    *reinterpret_cast<u32x4*>(&tile[prow(r0 + i) * S + d0]) = to_bf16x8<CT>(r, t.cache[i]);
-  }
-}
-
 template <int D>
 struct DqLds {
   static constexpr int S = D + 8;
@@ -97,9 +51,6 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   constexpr int S = DqLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
-  constexpr int CH = D / 8;
-  constexpr int NT = 16 * CH;
-  constexpr int ESZ = (CT == kQ8) ? 1 : 2;
   constexpr int ROWS = 32 * NW;
 
   const int tid = threadIdx.x;
@@ -131,7 +82,6 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   const int n_tiles = (key_end + BN - 1) / BN;
   const int tb = (int)((int64_t)split * n_tiles / SPL);
   const int te = (int)((int64_t)(split + 1) * n_tiles / SPL);
-  const int n_fast = P / BN;
 
   bf16x8 qreg[NKS], oreg[NKS];
   {
@@ -145,32 +95,8 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
   const float lse2 = p.lse[qrow] * kLog2e;
-  const bool stage_k = tid < NT;
-  const bool stage_v = tid >= 256 && tid < 256 + NT;
-  const bool stager = stage_k || stage_v;
-  const int task = stage_k ? tid : tid - 256;
-  const int tr0 = (task / CH) * 4, td0 = (task % CH) * 8;
-
   const int64_t bh = (int64_t)b * p.Hkv + kv;
-  const int64_t cap = p.cache.cap;
-  const char* cbase = static_cast<const char*>(stage_k ? p.cache.k : p.cache.v) + bh * cap * D * ESZ;
-  const uint16_t* cscale = (CT == kQ8) ? (stage_k ? p.cache.ks : p.cache.vs) + bh * cap * (D / 32)
-                                       : nullptr;
-  const uint16_t* chunk = (stage_k ? p.kc : p.vc) + bh * (int64_t)C * D;
-
-  Task4 raw;
-  auto issue = [&](int tile) {
-    if (tile < n_fast) {
-      load_fast<CT, D>(raw, cbase + (int64_t)tile * BN * D * ESZ,
-                       reinterpret_cast<const char*>(cscale + (int64_t)tile * BN * (D / 32)),
-                       tr0, td0);
-    } else {
-      load_general<CT, D>(raw, cbase, cscale, chunk, P, C, (int64_t)tile * BN + tr0, td0);
-    }
-  };
-  auto stage = [&](int buf) {
-    store_rows<CT, S>(stage_k ? sm.k[buf] : sm.v[buf], raw, tr0, td0);
-  };
+  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, p.P, p.C);
 
   const int k_off = prow(l32) * S + hf * 8;
   const TrOffsets t_off = tr_lane_offsets<S>(lane);
@@ -180,7 +106,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   const int lim = P + t;
 
-  if (tb < te && stager) issue(tb);
+  if (tb < te) stg.issue(tb);
   // delta = rowsum(dO * O) of this lane's row: each lane-half holds half of the dO
   // row (the B-operand layout), so read the same half of O and add the halves.
   float dlt;  // computed while the first tile is in flight
@@ -193,17 +119,16 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sdot = fmaf((float)ov[e], (float)oreg[ks][e], sdot);
     }
-    dlt = sdot + wave_xor32(sdot);
+    dlt = pair_sum(sdot);
     if (split == 0 && row_ok && hf == 0) p.delta[qrow] = dlt;  // read by bwd_dkdv
   }
 
   if (tb < te) {
-    if (stager) {
-      stage(0);
-      if (tb + 1 < te) issue(tb + 1);
-    }
+    stg.store(sm.k[0], sm.v[0]);
+    if (tb + 1 < te) stg.issue(tb + 1);
     __syncthreads();
   }
+  wait_global_loads();
   for (int tile = tb; tile < te; ++tile) {
     const int cur = (tile - tb) & 1;
     const uint16_t* kt = sm.k[cur];
@@ -243,10 +168,8 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
     }
 
     if (tile + 1 < te) {
-      if (stager) {
-        stage(cur ^ 1);
-        if (tile + 2 < te) issue(tile + 2);
-      }
+      stg.store(sm.k[cur ^ 1], sm.v[cur ^ 1]);
+      if (tile + 2 < te) stg.issue(tile + 2);
       __syncthreads();
     }
   }

@@ -39,7 +39,7 @@ namespace {
 constexpr int BN = kKeysPerTile;   // keys per tile
 constexpr int NW = kWavesPerBlock; // waves per workgroup
 constexpr int NTHR = 64 * NW;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kSumLimit = 256.f;  // bound on a lane's partial row sum of one tile
 
 template <int D>
 struct FwdLds {
@@ -48,63 +48,12 @@ struct FwdLds {
   uint16_t v[2][BN * S];
 };
 
-// Raw rows of one staging task: 4 key rows x 8 values, as loaded from HBM.
-struct Task4 {
-  u32x4 w[4];
-  bool cache[4];
-};
-
-// Load task rows j0 .. j0+3 (8 values from column d0) of a tile lying wholly in the
-// cache: `base` points at row 0 of the tile.
-template <int CT, int D>
-__device__ __forceinline__ void load_fast(Task4& t, const char* base, const char* sbase,
-                                          int r0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (CT == kQ8) {
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + (r0 + i) * D + d0);
-      const uint32_t s =
-          *reinterpret_cast<const uint16_t*>(sbase + ((r0 + i) * (D / 32) + (d0 >> 5)) * 2);
-      t.w[i] = u32x4{c.x, c.y, s, 0u};
-    } else {
-      t.w[i] = *reinterpret_cast<const u32x4*>(base + ((r0 + i) * D + d0) * 2);
-    }
-    t.cache[i] = true;
-  }
-}
-
-template <int CT, int D>
-__device__ __forceinline__ void load_general(Task4& t, const void* cache_base,
-                                             const uint16_t* cache_scale,
-                                             const uint16_t* chunk_base, int64_t P, int64_t C,
-                                             int64_t j0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    RawRow8 r;
-    t.cache[i] = load_row8<CT, D>(r, cache_base, cache_scale, chunk_base, P, C, j0 + i, d0);
-    t.w[i] = r.w;
-  }
-}
-
-template <int CT, int S>
-__device__ __forceinline__ void store_rows(uint16_t* tile, const Task4& t, int r0, int d0) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    RawRow8 r;
-    r.w = t.w[i];
-    *reinterpret_cast<u32x4*>(&tile[prow(r0 + i) * S + d0]) = to_bf16x8<CT>(r, t.cache[i]);
-  }
-}
-
 template <int D, int CT>
 __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   __shared__ __align__(16) FwdLds<D> sm;
   constexpr int S = FwdLds<D>::S;
   constexpr int NKS = D / 16;   // k-steps over head_dim
   constexpr int NDB = D / 32;   // 32-row blocks of O^T
-  constexpr int CH = D / 8;     // 8-value chunks per row
-  constexpr int NT = 16 * CH;   // staging tasks per tensor (4 rows x 8 values each)
-  constexpr int ESZ = (CT == kQ8) ? 1 : 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -136,7 +85,6 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   const int n_tiles = (key_end + BN - 1) / BN;
   const int tb = (int)((int64_t)split * n_tiles / SPL);
   const int te = (int)((int64_t)(split + 1) * n_tiles / SPL);
-  const int n_fast = P / BN;  // tiles [0, n_fast) lie wholly in the cache
 
   bf16x8 qreg[NKS];
   {
@@ -146,30 +94,8 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
       qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
 
-  // Staging role: threads [0, NT) stage K, threads [256, 256 + NT) stage V.
-  const bool stage_k = tid < NT;
-  const bool stage_v = tid >= 256 && tid < 256 + NT;
-  const bool stager = stage_k || stage_v;
-  const int task = stage_k ? tid : tid - 256;
-  const int tr0 = (task / CH) * 4, td0 = (task % CH) * 8;  // task rows tr0..tr0+3, cols td0..
-
   const int64_t bh = (int64_t)b * p.Hkv + kv;
-  const int64_t cap = p.cache.cap;
-  const char* cbase = static_cast<const char*>(stage_k ? p.cache.k : p.cache.v) + bh * cap * D * ESZ;
-  const uint16_t* cscale = (CT == kQ8) ? (stage_k ? p.cache.ks : p.cache.vs) + bh * cap * (D / 32)
-                                       : nullptr;
-  const uint16_t* chunk = (stage_k ? p.kc : p.vc) + bh * (int64_t)C * D;
-
-  Task4 raw;
-  auto issue = [&](int tile) {
-    if (tile < n_fast) {
-      load_fast<CT, D>(raw, cbase + (int64_t)tile * BN * D * ESZ,
-                       reinterpret_cast<const char*>(cscale + (int64_t)tile * BN * (D / 32)),
-                       tr0, td0);
-    } else {
-      load_general<CT, D>(raw, cbase, cscale, chunk, P, C, (int64_t)tile * BN + tr0, td0);
-    }
-  };
+  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, p.P, p.C);
 
   // Per-lane LDS offsets of the MFMA operands.
   const int k_off = prow(l32) * S + hf * 8;   // + kb*32*S + ks*16
@@ -179,8 +105,8 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
   float m = -INFINITY, l = 0.f;
+  float mc = 0.f;                           // m * c, or 0 while m is unset
   const float c = p.scale_log2;
-  const float thr = kRescaleThreshold / c;  // raise the max only past m + thr
   const int lim = P + t;                    // this row may attend keys 0..lim
 
   // MFMA blocks run at raised wave priority: when both waves of a SIMD are ready,
@@ -199,8 +125,27 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // Online softmax of one tile: updates m, l (and rescales acc when the max grows),
-  // returns the probabilities as the bf16 B operands of P V.
+  // Online softmax of one tile. The probabilities are taken against the running
+  // reference m first; the exact row max is needed only when that reference is
+  // unset or too low, which the tile's partial row sum shows: it exceeds
+  // kSumLimit whenever some probability does. Then m is raised to the row max,
+  // the accumulator rescaled and the tile's probabilities recomputed. Returns the
+  // probabilities as the bf16 B operands of P V.
+  auto probs = [&](const f32x16 (&st)[2], bf16x8 (&pb)[4]) {
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -mc)),
+                                     __builtin_amdgcn_exp2f(fmaf(st[kb][i + 1], c, -mc)));
+        lt = add_bf16_pair(w, lt);
+        const bf16x2 pr = __builtin_bit_cast(bf16x2, w);
+        pb[kb * 2 + (i >> 3)][i & 7] = pr[0];
+        pb[kb * 2 + (i >> 3)][(i & 7) + 1] = pr[1];
+      }
+    return lt;
+  };
   auto softmax = [&](f32x16 (&st)[2], int tile, bf16x8 (&pb)[4]) {
     const int kbase = tile * BN;
     if (kbase + BN - 1 > P + t_min) {
@@ -211,32 +156,26 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kb][i] = -INFINITY;
     }
-    float mt = -INFINITY;
+    float lt = probs(st, pb);
+    if (__builtin_amdgcn_ballot_w64(lt > kSumLimit || m == -INFINITY) != 0) {
+      float mt = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb][i]);
-    mt = fmaxf(mt, wave_xor32(mt));
-    const bool grow = mt > m + thr;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb][i]);
+      const float mn = fmaxf(m, pair_max(mt));
       // alpha = 1 for rows that keep their max; 0 for rows leaving -inf.
-      const float alpha = grow ? __builtin_amdgcn_exp2f((m - mt) * c) : 1.f;
+      const float alpha = (mn == m) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * c);
       l *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-      m = grow ? mt : m;
+      m = mn;
+      mc = (m == -INFINITY) ? 0.f : m * c;
+      lt = probs(st, pb);
     }
-    const float mc = (m == -INFINITY) ? 0.f : m * c;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -mc));
-        l += pv;
-        pb[kb * 2 + (i >> 3)][i & 7] = (__bf16)pv;
-      }
+    l += lt;
   };
   auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4]) {
     __builtin_amdgcn_s_setprio(1);
@@ -249,13 +188,12 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   };
 
   if (tb < te) {
-    if (stager) {
-      issue(tb);
-      store_rows<CT, S>(stage_k ? sm.k[0] : sm.v[0], raw, tr0, td0);
-      if (tb + 1 < te) issue(tb + 1);
-    }
+    stg.issue(tb);
+    stg.store(sm.k[0], sm.v[0]);
+    if (tb + 1 < te) stg.issue(tb + 1);
     __syncthreads();
   }
+  wait_global_loads();
   for (int tile = tb; tile < te; ++tile) {
     const int cur = (tile - tb) & 1;
     f32x16 st[2];
@@ -264,15 +202,13 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
     softmax(st, tile, pb);
     pv_mfma(sm.v[cur], pb);
     if (tile + 1 < te) {
-      if (stager) {
-        store_rows<CT, S>(stage_k ? sm.k[cur ^ 1] : sm.v[cur ^ 1], raw, tr0, td0);
-        if (tile + 2 < te) issue(tile + 2);
-      }
+      stg.store(sm.k[cur ^ 1], sm.v[cur ^ 1]);
+      if (tile + 2 < te) stg.issue(tile + 2);
       __syncthreads();
     }
   }
 
-  const float l_tot = l + wave_xor32(l);
+  const float l_tot = pair_sum(l);
   if (!row_ok) return;
   if (SPL == 1) {
     const float inv = 1.f / l_tot;

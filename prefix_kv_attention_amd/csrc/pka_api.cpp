@@ -156,8 +156,8 @@ static Plan make_plan(const pka_dims& d) {
   pl.n_rb = (int)((G * d.chunk_len + kRowsPerBlock - 1) / kRowsPerBlock);
   const int64_t units = (int64_t)d.batch * d.n_heads_kv * pl.n_rb;
   int64_t split = 1;
-  if (units < kNumCUs) {
-    split = kNumCUs / units;
+  if (units < kNumCUs * kBlocksPerCU) {
+    split = kNumCUs * kBlocksPerCU / units;
     const int64_t min_tiles = (d.prefix_len + 1 + kKeysPerTile - 1) / kKeysPerTile;
     const int64_t max_split = min_tiles / 8 > 1 ? min_tiles / 8 : 1;
     if (split > max_split) split = max_split;

@@ -132,8 +132,29 @@ __device__ __forceinline__ int xcd_logical_id(int i, int nblk) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-__device__ __forceinline__ float wave_xor32(float v) {
-  return __shfl_xor(v, 32, 64);
+// Wait until every global load this wave issued has returned (s_waitcnt vmcnt(0)).
+// Used once after a kernel's prologue: the compiler cannot tell at the loop header
+// whether the one-time operand loads (Q, dO) are still in flight, and otherwise
+// inserts waits inside the loop that also stall on the next tile's prefetch.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Lane l and lane l ^ 32 hold the two halves of one row: sum / max of the pair,
+// returned to both lanes (v_permlane32_swap, no LDS round trip).
+__device__ __forceinline__ float pair_sum(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Sum of a packed bf16 pair, accumulated in fp32 (v_dot2c_f32_bf16 with (1, 1)).
+__device__ __forceinline__ float add_bf16_pair(uint32_t packed, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -184,5 +205,104 @@ __device__ __forceinline__ bf16x8 lds_tr_operand(const uint16_t* tile, const TrO
   const v8i16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// ---------------------------------------------------------------------------
+// Staging of one tile of 64 keys of K and V, [cache rows 0..P-1 ; chunk rows],
+// from HBM into two row-major LDS tiles (layout below). The work is 2 * NT tasks of
+// 4 rows x 8 values (NT per tensor); thread tid takes tasks tid + s * NTHR. Loads
+// go to registers first (issue) so that they overlap the compute of the current
+// tile, and are converted to bf16 when written to LDS (store).
+struct Task4 {
+  u32x4 w[4];
+  bool cache[4];
+};
+
+template <int CT, int D, int NTHR>
+struct KVStager {
+  static constexpr int BN = kKeysPerTile;
+  static constexpr int CH = D / 8;
+  static constexpr int NT = (BN / 4) * CH;             // tasks per tensor
+  static constexpr int TPT = (2 * NT + NTHR - 1) / NTHR;  // task slots per thread
+  static constexpr int ESZ = (CT == kQ8) ? 1 : 2;
+  static constexpr int S = D + 8;
+
+  const char* cbase[TPT];
+  const uint16_t* cscale[TPT];
+  const uint16_t* chunk[TPT];
+  int tr0[TPT], td0[TPT];
+  bool active[TPT], is_k[TPT];
+  Task4 raw[TPT];
+  int64_t P, C;
+  int n_fast;  // tiles [0, n_fast) lie wholly in the cache
+
+  __device__ __forceinline__ KVStager(int tid, const CacheRef& cache, const uint16_t* kc,
+                                      const uint16_t* vc, int64_t bh, int64_t P_,
+                                      int64_t C_) {
+    P = P_;
+    C = C_;
+    n_fast = (int)(P_ / BN);
+#pragma unroll
+    for (int s = 0; s < TPT; ++s) {
+      const int task = tid + s * NTHR;
+      is_k[s] = task < NT;
+      active[s] = task < 2 * NT;
+      const int tk = is_k[s] ? task : task - NT;
+      tr0[s] = (tk / CH) * 4;
+      td0[s] = (tk % CH) * 8;
+      cbase[s] = static_cast<const char*>(is_k[s] ? cache.k : cache.v) + bh * cache.cap * D * ESZ;
+      cscale[s] = (CT == kQ8) ? (is_k[s] ? cache.ks : cache.vs) + bh * cache.cap * (D / 32)
+                              : nullptr;
+      chunk[s] = (is_k[s] ? kc : vc) + bh * C_ * D;
+    }
+  }
+
+  __device__ __forceinline__ void issue(int tile) {
+#pragma unroll
+    for (int s = 0; s < TPT; ++s) {
+      if (!active[s]) continue;
+      Task4& t = raw[s];
+      if (tile < n_fast) {
+        const char* base = cbase[s] + (int64_t)tile * BN * D * ESZ;
+        const char* sbase = reinterpret_cast<const char*>(cscale[s] + (int64_t)tile * BN * (D / 32));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = tr0[s] + i;
+          if constexpr (CT == kQ8) {
+            const u32x2 c = *reinterpret_cast<const u32x2*>(base + r * D + td0[s]);
+            const uint32_t sc =
+                *reinterpret_cast<const uint16_t*>(sbase + (r * (D / 32) + (td0[s] >> 5)) * 2);
+            t.w[i] = u32x4{c.x, c.y, sc, 0u};
+          } else {
+            t.w[i] = *reinterpret_cast<const u32x4*>(base + (r * D + td0[s]) * 2);
+          }
+          t.cache[i] = true;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          RawRow8 r;
+          t.cache[i] = load_row8<CT, D>(r, cbase[s], cscale[s], chunk[s], P, C,
+                                        (int64_t)tile * BN + tr0[s] + i, td0[s]);
+          t.w[i] = r.w;
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(uint16_t* ktile, uint16_t* vtile) const {
+#pragma unroll
+    for (int s = 0; s < TPT; ++s) {
+      if (!active[s]) continue;
+      uint16_t* tile = is_k[s] ? ktile : vtile;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        RawRow8 r;
+        r.w = raw[s].w[i];
+        *reinterpret_cast<u32x4*>(&tile[prow(tr0[s] + i) * S + td0[s]]) =
+            to_bf16x8<CT>(r, raw[s].cache[i]);
+      }
+    }
+  }
+};
 
 }  // namespace pka

@@ -9,7 +9,11 @@
 namespace pka {
 
 // Tile geometry shared by host planning and kernels.
-constexpr int kWavesPerBlock = 8;   // waves per forward / dQ workgroup
+#ifndef PKA_WAVES_PER_BLOCK
+#define PKA_WAVES_PER_BLOCK 8
+#endif
+constexpr int kWavesPerBlock = PKA_WAVES_PER_BLOCK;   // waves per forward / dQ workgroup
+constexpr int kBlocksPerCU = 8 / kWavesPerBlock;      // resident forward / dQ workgroups per CU
 constexpr int kRowsPerBlock = 32 * kWavesPerBlock;  // packed query rows per workgroup
 constexpr int kKeysPerTile = 64;    // keys staged in LDS per step
 constexpr int kDkvKeysPerBlock = 64;   // chunk keys per dK/dV workgroup (2 x 32)
