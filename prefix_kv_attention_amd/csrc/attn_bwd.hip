@@ -129,6 +129,9 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
     __syncthreads();
   }
   wait_global_loads();
+  f32x16 ndlt;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ndlt[i] = -dlt;
   for (int tile = tb; tile < te; ++tile) {
     const int cur = (tile - tb) & 1;
     const uint16_t* kt = sm.k[cur];
@@ -137,7 +140,8 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
     const bool masked = kbase + BN - 1 > P + t_min;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 st = f32x16{}, dpt = f32x16{};
+      // dP^T starts from -delta (this lane's row), so the chain yields dP - delta.
+      f32x16 st = f32x16{}, dpt = ndlt;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
@@ -156,7 +160,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = __builtin_amdgcn_exp2f(fmaf(st[i], c, -lse2));
-        dsb[i >> 3][i & 7] = (__bf16)(pv * (dpt[i] - dlt));
+        dsb[i >> 3][i & 7] = (__bf16)(pv * dpt[i]);
       }
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll

@@ -256,12 +256,18 @@ struct KVStager {
     }
   }
 
-  __device__ __forceinline__ void issue(int tile) {
+  // Load the K rows of tile tk and the V rows of tile tv into registers; a
+  // negative index loads nothing for that tensor. fast: both tiles lie wholly in
+  // the cache (uniform base pointer, no per-row checks).
+  template <bool FAST>
+  __device__ __forceinline__ void issue(int tk, int tv) {
 #pragma unroll
     for (int s = 0; s < TPT; ++s) {
       if (!active[s]) continue;
+      const int tile = is_k[s] ? tk : tv;
+      if (!FAST && tile < 0) continue;
       Task4& t = raw[s];
-      if (tile < n_fast) {
+      if (FAST || tile < n_fast) {
         const char* base = cbase[s] + (int64_t)tile * BN * D * ESZ;
         const char* sbase = reinterpret_cast<const char*>(cscale[s] + (int64_t)tile * BN * (D / 32));
 #pragma unroll
@@ -288,12 +294,15 @@ struct KVStager {
       }
     }
   }
+  __device__ __forceinline__ void issue(int tile) { issue<false>(tile, tile); }
 
+  // Convert and write the loaded rows; a null tile skips that tensor.
   __device__ __forceinline__ void store(uint16_t* ktile, uint16_t* vtile) const {
 #pragma unroll
     for (int s = 0; s < TPT; ++s) {
       if (!active[s]) continue;
       uint16_t* tile = is_k[s] ? ktile : vtile;
+      if (tile == nullptr) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         RawRow8 r;
