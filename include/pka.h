@@ -72,15 +72,25 @@ typedef enum {
                          value = f32(scale) * code, read as bf16 (RNE)            */
 } pka_cache_type;
 
-/* One chunk step, uniform over the B windows. */
+/* One chunk step of B windows. Every window has the same chunk length; the prefix
+ * length is the same for all windows unless prefix_lens is given (ragged windows:
+ * a batch of windows walked to different depths, the longest one setting the
+ * work, as in "train: walk the window", Contents: the longest window's step). */
 typedef struct {
   int32_t batch;       /* B >= 1                                    */
   int32_t n_heads_q;   /* Hq >= 1, a multiple of n_heads_kv         */
   int32_t n_heads_kv;  /* Hkv >= 1                                  */
   int32_t head_dim;    /* D: 64 or 128                              */
-  int64_t prefix_len;  /* P >= 0: cached context rows 0..P-1 are read */
+  int64_t prefix_len;  /* P >= 0: cached context rows 0..P-1 are read; with
+                          prefix_lens, the largest prefix of the batch          */
   int64_t chunk_len;   /* C >= 1                                    */
   float softmax_scale; /* > 0 and finite; usually 1/sqrt(D)         */
+  const int32_t* prefix_lens; /* optional DEVICE array int32[B] (4-byte aligned):
+                          window b's own prefix length P_b; chunk row i of window
+                          b then attends to cache rows 0..P_b-1 and chunk rows
+                          0..i, and appends write rows [P_b, P_b + C). Entries are
+                          clamped to [0, prefix_len] (never read past prefix_len).
+                          NULL: every window has prefix_len.                     */
 } pka_dims;
 
 /* The frozen prefix cache of B windows x Hkv heads x capacity token rows. */
@@ -131,7 +141,8 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
 /* Re-decode of the chunk into the cache ("train: walk the window", What it is and
  * Contents): writes cache rows [P, P+C) of every (window, KV head) from k, v
  * (bf16 [B][Hkv][C][D]). Uses batch, n_heads_kv, head_dim, prefix_len, chunk_len of
- * dims; requires P + C <= capacity and a cache of the matching type.
+ * dims (rows [P_b, P_b+C) with prefix_lens); requires prefix_len + C <= capacity
+ * and a cache of the matching type.
  *  q8_0: per block of 32 values along D: amax = max|x|, d = amax/127 (IEEE fp32
  *        division), scale = fp16(d) (RNE), code = clamp(round_half_away(x/d), +-127)
  *        with the fp32 d; an all-zero block stores scale 0 and codes 0.

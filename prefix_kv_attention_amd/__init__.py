@@ -10,7 +10,12 @@ Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
 ``kv_append_bf16``, ``kv_dequant_q8_0``, ``fwd_workspace_bytes``,
 ``bwd_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
-constants: "train: walk the window", Why it's a draft).
+constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
+chunk loop of a batch of windows: step, append, advance every window's prefix.
+
+Every call takes ``prefix_len`` (an int: the prefix of every window, or the
+largest one) and optionally ``prefix_lens``, a CUDA int32 tensor [B] of the
+windows' own prefix lengths (ragged windows; entries clamped to [0, prefix_len]).
 """
 from __future__ import annotations
 
@@ -39,7 +44,7 @@ class Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("n_heads_q", ctypes.c_int32),
                 ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("prefix_len", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("prefix_lens", ctypes.c_void_p)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -96,9 +101,15 @@ def _stream(device):
 
 
 def make_dims(batch, n_heads_q, n_heads_kv, head_dim, prefix_len, chunk_len,
-              softmax_scale) -> Dims:
+              softmax_scale, prefix_lens=None) -> Dims:
+    if prefix_lens is not None:
+        if (prefix_lens.dtype != torch.int32 or not prefix_lens.is_cuda
+                or not prefix_lens.is_contiguous() or prefix_lens.numel() != int(batch)):
+            raise ValueError("prefix_lens must be a contiguous CUDA int32 tensor of "
+                             f"{int(batch)} entries")
     return Dims(int(batch), int(n_heads_q), int(n_heads_kv), int(head_dim),
-                int(prefix_len), int(chunk_len), float(softmax_scale))
+                int(prefix_len), int(chunk_len), float(softmax_scale),
+                None if prefix_lens is None else prefix_lens.data_ptr())
 
 
 class PrefixCache:
@@ -132,10 +143,10 @@ class PrefixCache:
                          self.v_scale.data_ptr() if self.v_scale is not None else None)
 
 
-def _chunk_dims(q, k, prefix_len, scale):
+def _chunk_dims(q, k, prefix_len, scale, prefix_lens=None):
     B, Hq, C, D = q.shape
     Hkv = k.shape[1]
-    return make_dims(B, Hq, Hkv, D, prefix_len, C, scale)
+    return make_dims(B, Hq, Hkv, D, prefix_len, C, scale, prefix_lens)
 
 
 def _need(t, name, dtype=torch.bfloat16):
@@ -158,11 +169,11 @@ def _workspace(nbytes, device):
 
 
 def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
-                   o=None, lse=None, ws=None):
+                   o=None, lse=None, ws=None, prefix_lens=None):
     """O [B][Hq][C][D] bf16 and LSE [B][Hq][C] f32 of the chunk against the prefix."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
-    dims = _chunk_dims(q, k, prefix_len, scale)
+    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
@@ -178,12 +189,12 @@ def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
 
 
 def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o, lse,
-                   d_o, dq=None, dk=None, dv=None, delta=None, ws=None):
+                   d_o, dq=None, dk=None, dv=None, delta=None, ws=None, prefix_lens=None):
     """dQ (chunk rows), dK and dV (the chunk's own keys); the prefix gets nothing."""
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
         _need(t, n)
     _need(lse, "lse", torch.float32)
-    dims = _chunk_dims(q, k, prefix_len, scale)
+    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
@@ -198,32 +209,34 @@ def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o
     return dq, dk, dv
 
 
-def _append(fn, name, k, v, cache: PrefixCache, prefix_len: int):
+def _append(fn, name, k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
     _need(k, "k")
     _need(v, "v")
     B, Hkv, C, D = k.shape
-    dims = make_dims(B, Hkv, Hkv, D, prefix_len, C, 1.0)
+    dims = make_dims(B, Hkv, Hkv, D, prefix_len, C, 1.0, prefix_lens)
     cd = cache.desc()
     _check(fn(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(cd), _stream(k.device)), name)
 
 
-def kv_append_q8_0(k, v, cache: PrefixCache, prefix_len: int):
+def kv_append_q8_0(k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
     """Quantise the chunk's K/V (bf16 [B][Hkv][C][D]) into cache rows [P, P+C)."""
-    _append(_lib.pka_kv_append_q8_0, "pka_kv_append_q8_0", k, v, cache, prefix_len)
+    _append(_lib.pka_kv_append_q8_0, "pka_kv_append_q8_0", k, v, cache, prefix_len,
+            prefix_lens)
 
 
-def kv_append_f16(k, v, cache: PrefixCache, prefix_len: int):
-    _append(_lib.pka_kv_append_f16, "pka_kv_append_f16", k, v, cache, prefix_len)
+def kv_append_f16(k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
+    _append(_lib.pka_kv_append_f16, "pka_kv_append_f16", k, v, cache, prefix_len, prefix_lens)
 
 
-def kv_append_bf16(k, v, cache: PrefixCache, prefix_len: int):
-    _append(_lib.pka_kv_append_bf16, "pka_kv_append_bf16", k, v, cache, prefix_len)
+def kv_append_bf16(k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
+    _append(_lib.pka_kv_append_bf16, "pka_kv_append_bf16", k, v, cache, prefix_len,
+            prefix_lens)
 
 
-def kv_append(k, v, cache: PrefixCache, prefix_len: int):
+def kv_append(k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
     """Append in the cache's own storage type."""
     {"q8_0": kv_append_q8_0, "f16": kv_append_f16, "bf16": kv_append_bf16}[
-        cache.cache_type](k, v, cache, prefix_len)
+        cache.cache_type](k, v, cache, prefix_len, prefix_lens)
 
 
 def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = True):
@@ -240,23 +253,76 @@ def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = 
 
 class _ChunkAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, cache, prefix_len, scale):
-        o, lse = chunk_attn_fwd(q, k, v, cache, prefix_len, scale)
+    def forward(ctx, q, k, v, cache, prefix_len, scale, prefix_lens):
+        o, lse = chunk_attn_fwd(q, k, v, cache, prefix_len, scale, prefix_lens=prefix_lens)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.cache, ctx.prefix_len, ctx.scale = cache, prefix_len, scale
+        ctx.prefix_lens = prefix_lens
         return o
 
     @staticmethod
     def backward(ctx, d_o):
         q, k, v, o, lse = ctx.saved_tensors
         dq, dk, dv = chunk_attn_bwd(q, k, v, ctx.cache, ctx.prefix_len, ctx.scale, o, lse,
-                                    d_o.contiguous())
-        return dq, dk, dv, None, None, None
+                                    d_o.contiguous(), prefix_lens=ctx.prefix_lens)
+        return dq, dk, dv, None, None, None, None
 
 
-def chunk_attention(q, k, v, cache: PrefixCache, prefix_len: int, scale: float):
+def chunk_attention(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
+                    prefix_lens=None):
     """Autograd op: O of the chunk; gradients reach q, k, v only (never the cache)."""
-    return _ChunkAttention.apply(q, k, v, cache, prefix_len, scale)
+    return _ChunkAttention.apply(q, k, v, cache, prefix_len, scale, prefix_lens)
+
+
+class WindowWalk:
+    """The chunk loop over a batch of windows ("train: walk the window", What it is and
+    Contents): each step trains one chunk of every window against that window's cached
+    prefix, then re-decodes the chunk into the cache and advances the prefix by C.
+
+    Windows may start at different prefix lengths (ragged). The device tensor of the
+    per-window lengths and the host-side maximum are kept in step; the caller owns the
+    cache, whose capacity bounds the walk.
+    """
+
+    def __init__(self, cache: PrefixCache, prefix_lens, scale: float):
+        self.cache = cache
+        self.scale = float(scale)
+        self.lens = [int(p) for p in prefix_lens]
+        if len(self.lens) != cache.batch or min(self.lens) < 0:
+            raise ValueError("one non-negative prefix length per window of the cache")
+        self._dev = torch.tensor(self.lens, dtype=torch.int32, device=cache.k.device)
+
+    @property
+    def prefix_len(self) -> int:
+        return max(self.lens)
+
+    def _plens(self):
+        return None if len(set(self.lens)) == 1 else self._dev
+
+    def forward(self, q, k, v):
+        return chunk_attn_fwd(q, k, v, self.cache, self.prefix_len, self.scale,
+                              prefix_lens=self._plens())
+
+    def backward(self, q, k, v, o, lse, d_o, delta=None):
+        return chunk_attn_bwd(q, k, v, self.cache, self.prefix_len, self.scale, o, lse, d_o,
+                              delta=delta, prefix_lens=self._plens())
+
+    def advance(self, k, v):
+        """Append the chunk's K/V at every window's prefix end, then P_b += C."""
+        C = k.shape[2]
+        if self.prefix_len + C > self.cache.capacity:
+            raise ValueError(f"cache capacity {self.cache.capacity} < "
+                             f"{self.prefix_len + C} rows")
+        kv_append(k, v, self.cache, self.prefix_len, prefix_lens=self._plens())
+        self.lens = [p + C for p in self.lens]
+        self._dev += C
+
+    def step(self, q, k, v, d_o):
+        """Forward, backward and append of one chunk: (o, lse, dq, dk, dv)."""
+        o, lse = self.forward(q, k, v)
+        dq, dk, dv = self.backward(q, k, v, o, lse, d_o)
+        self.advance(k, v)
+        return o, lse, dq, dk, dv
 
 
 def profile_enable(on: bool = True):

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int G = p.G;
   const int C = (int)p.C;
-  const int P = (int)p.P;
+  const int P = (int)window_prefix(p.plens, b, p.P);  // this window's prefix
   const int rows = G * C;
 
   const int r = rb * ROWS + wave * 32 + l32;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   const float c = p.scale_log2;
   const float lse2 = p.lse[qrow] * kLog2e;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
-  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, p.P, p.C);
+  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, P, p.C);
 
   const int k_off = prow(l32) * S + hf * 8;
   const TrOffsets t_off = tr_lane_offsets<S>(lane);

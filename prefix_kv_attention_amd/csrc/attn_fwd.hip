@@ -67,7 +67,7 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int G = p.G;
   const int C = (int)p.C;
-  const int P = (int)p.P;
+  const int P = (int)window_prefix(p.plens, b, p.P);  // this window's prefix
   const int rows = G * C;
   constexpr int ROWS = 32 * NW;
 
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   }
 
   const int64_t bh = (int64_t)b * p.Hkv + kv;
-  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, p.P, p.C);
+  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, P, p.C);
 
   // Per-lane LDS offsets of the MFMA operands.
   const int k_off = prow(l32) * S + hf * 8;   // + kb*32*S + ks*16

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void append_q8_0_kernel(AppendParams p) {
     }
     q[c >> 2][c & 3] = w;
   }
-  const int64_t crow = bh * p.cap + p.P + tok;
+  const int64_t crow = bh * p.cap + window_prefix(p.plens, (int)(bh / p.Hkv), p.P) + tok;
   int8_t* dst = static_cast<int8_t*>(is_v ? p.cv : p.ck) + crow * D + blk * 32;
   reinterpret_cast<u32x4*>(dst)[0] = q[0];
   reinterpret_cast<u32x4*>(dst)[1] = q[1];
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void append_16_kernel(AppendParams p) {
   } else {
     o = w;
   }
-  const int64_t crow = bh * p.cap + p.P + tok;
+  const int64_t crow = bh * p.cap + window_prefix(p.plens, (int)(bh / p.Hkv), p.P) + tok;
   *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(is_v ? p.cv : p.ck) + crow * p.D + c8 * 8) = o;
 }
 

@@ -54,6 +54,8 @@ pka_status check_dims(const pka_dims* d) {
     return fail(PKA_ERR_DIMS, "group * chunk_len exceeds 2^31 - 1");
   if (!(d->softmax_scale > 0.f) || !std::isfinite(d->softmax_scale))
     return fail(PKA_ERR_DIMS, "softmax_scale must be finite and > 0");
+  if ((reinterpret_cast<uintptr_t>(d->prefix_lens) & 3u) != 0)
+    return fail(PKA_ERR_ALIGN, "prefix_lens not 4-byte aligned");
   return PKA_OK;
 }
 
@@ -261,6 +263,7 @@ pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k
   p.Hkv = dims->n_heads_kv;
   p.G = dims->n_heads_q / dims->n_heads_kv;
   p.P = dims->prefix_len;
+  p.plens = dims->prefix_lens;
   p.C = dims->chunk_len;
   p.scale = dims->softmax_scale;
   p.scale_log2 = (float)((double)dims->softmax_scale * 1.4426950408889634);
@@ -309,6 +312,7 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
   p.Hkv = dims->n_heads_kv;
   p.G = dims->n_heads_q / dims->n_heads_kv;
   p.P = dims->prefix_len;
+  p.plens = dims->prefix_lens;
   p.C = dims->chunk_len;
   p.scale = dims->softmax_scale;
   p.scale_log2 = (float)((double)dims->softmax_scale * 1.4426950408889634);
@@ -340,6 +344,8 @@ static pka_status append_common(const pka_dims* dims, const void* k, const void*
     return fail(PKA_ERR_DIMS, "prefix_len must be >= 0 and chunk_len >= 1");
   if (dims->prefix_len > kMaxSeq - dims->chunk_len)
     return fail(PKA_ERR_DIMS, "prefix_len + chunk_len exceeds 2^31 - 1");
+  if ((reinterpret_cast<uintptr_t>(dims->prefix_lens) & 3u) != 0)
+    return fail(PKA_ERR_ALIGN, "prefix_lens not 4-byte aligned");
   if ((st = check_ptrs({k, v}, "k, v")) != PKA_OK) return st;
   if ((st = check_cache(cache, dims, dims->prefix_len + dims->chunk_len, true)) != PKA_OK) return st;
   if (cache->type != want_type)
@@ -355,7 +361,9 @@ static pka_status append_common(const pka_dims* dims, const void* k, const void*
   p.rows = (int64_t)dims->batch * dims->n_heads_kv * dims->chunk_len;
   p.C = dims->chunk_len;
   p.P = dims->prefix_len;
+  p.plens = dims->prefix_lens;
   p.cap = cache->capacity;
+  p.Hkv = dims->n_heads_kv;
   p.D = dims->head_dim;
   hipError_t e = launch_append(p, want_type, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv_append launch");

@@ -121,6 +121,14 @@ __device__ __forceinline__ u32x4 to_bf16x8(const RawRow8& r, bool is_cache) {
   }
 }
 
+// Prefix length of window b: its entry of the optional per-window array, clamped to
+// [0, P] (P: the largest prefix, which bounds every cache access), else P.
+__device__ __forceinline__ int64_t window_prefix(const int32_t* plens, int b, int64_t P) {
+  if (plens == nullptr) return P;
+  const int64_t pb = plens[b];
+  return pb < 0 ? 0 : (pb > P ? P : pb);
+}
+
 // Workgroup order: hardware dispatches workgroup i to XCD i % 8. Renumber so each
 // XCD receives a contiguous range of logical ids; neighbouring logical ids read the
 // same K/V tiles and so share that XCD's L2.

@@ -47,7 +47,8 @@ struct FwdParams {
   float* ws_o;    // [n_split][B*Hq*C][D]  (only when n_split > 1)
   float* ws_lse;  // [n_split][B*Hq*C]
   int B, Hq, Hkv, G;
-  int64_t P, C;
+  int64_t P, C;      // P: the (largest) prefix length
+  const int32_t* plens;  // per-window prefix lengths (device) or null
   float scale;       // softmax scale
   float scale_log2;  // scale * log2(e)
   Plan plan;
@@ -69,6 +70,7 @@ struct BwdParams {
   float* ws_dkv;  // [n_dkv_split][2][B*Hkv*C][D] (only when n_dkv_split > 1)
   int B, Hq, Hkv, G;
   int64_t P, C;
+  const int32_t* plens;
   float scale;
   float scale_log2;
   Plan plan;
@@ -83,6 +85,8 @@ struct AppendParams {
   uint16_t* cvs;
   int64_t rows;  // B * Hkv * C
   int64_t C, P, cap;
+  const int32_t* plens;  // per-window prefix lengths (device) or null
+  int Hkv;
   int D;
 };
 

@@ -190,3 +190,34 @@ def test_workspace_plan(pka):
     assert pka.bwd_workspace_bytes(d3) >= nrow * 4 + 2 * nrow * 128 * 4
     # invalid dims -> 0
     assert pka.fwd_workspace_bytes(dims(pka, head_dim=80)) == 0
+
+
+def test_struct_layout_matches_the_header(pka, tmp_path):
+    """The ctypes mirrors of pka_dims and pka_cache have the C compiler's layout."""
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "pka.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu %zu %zu\\n", sizeof(pka_dims),'
+        " offsetof(pka_dims, prefix_len), offsetof(pka_dims, chunk_len),"
+        " offsetof(pka_dims, softmax_scale), offsetof(pka_dims, prefix_lens),"
+        " sizeof(pka_cache));\n  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    D = pka.Dims
+    want = [ctypes.sizeof(D), D.prefix_len.offset, D.chunk_len.offset, D.softmax_scale.offset,
+            D.prefix_lens.offset, ctypes.sizeof(pka.CacheDesc)]
+    assert got == want
+
+
+def test_prefix_lens_alignment_is_checked(pka):
+    """A misaligned per-window prefix array is refused before any launch."""
+    d = dims(pka)
+    d.prefix_lens = A + 2
+    st, msg = fwd(pka, d, cache(pka))
+    assert st == 5 and "prefix_lens" in msg
+    c = cache(pka, capacity=600, type=pka.CACHE_F16)
+    assert pka.lib.pka_kv_append_f16(ctypes.byref(d), A, A, ctypes.byref(c), None) == 5
