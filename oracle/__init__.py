@@ -16,7 +16,7 @@ hand-derived q8_0 blocks and an independent re-derivation of q8_0 with Python's 
 float and struct rounding. No function here is "parity unpinned".
 """
 from .attention import (  # noqa: F401
-    allowed_mask, kv_head_of, group_fwd, group_bwd, chunk_fwd, chunk_bwd,
+    allowed_mask, kv_head_of, group_fwd, group_bwd, group_bwd_prefix, chunk_fwd, chunk_bwd,
     full_causal_fwd, full_causal_bwd, softmax_probs,
 )
 from .cache import (  # noqa: F401

@@ -106,6 +106,35 @@ def group_bwd(q, kc, vc, kp, vp, scale, do):
     return dq, dkc, dvc, delta
 
 
+def group_bwd_prefix(q, kc, vc, kp, vp, scale, do):
+    """Gradient of the chunk's loss w.r.t. the cached prefix rows of one (window, KV
+    head), from the chunk queries only: dKp [P][D] and dVp [P][D].
+
+    The same masked softmax as group_bwd; every chunk row sees every prefix row, so
+    dKp = scale * sum_g dS_g[:, :P]^T Q_g and dVp = sum_g Pr_g[:, :P]^T dO_g. This is
+    the gradient a stop-gradient prefix discards ("train: walk the window", Why it's
+    a draft: the exact reverse pass with a horizon H; "stop-gradient through context
+    tokens", Mechanism: kept queries attend to context k/v, so context dK/dV are
+    nonzero and feed the k/v weight gradients).
+    """
+    q, kc, vc, kp, vp, do = (np.asarray(a, dtype=np.float64)
+                             for a in (q, kc, vc, kp, vp, do))
+    G, C, D = q.shape
+    P = kp.shape[0]
+    kf = np.concatenate([kp, kc], axis=0)
+    vf = np.concatenate([vp, vc], axis=0)
+    allowed = allowed_mask(P, C)
+    dkp = np.zeros((P, D))
+    dvp = np.zeros((P, D))
+    for g in range(G):
+        o, _, pr = _head_fwd(q[g], kf, vf, allowed, scale)
+        delta = (do[g] * o).sum(axis=1)
+        ds = pr * (do[g] @ vf.T - delta[:, None])
+        dkp += scale * (ds[:, :P].T @ q[g])
+        dvp += pr[:, :P].T @ do[g]
+    return dkp, dvp
+
+
 def _split(q, kc, n_heads_kv):
     B, Hq = q.shape[:2]
     return B, Hq, Hq // n_heads_kv
