@@ -138,6 +138,26 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
                               void* dv, float* delta, void* ws, size_t ws_bytes,
                               pka_stream_t stream);
 
+/* Gradient of the chunk's loss with respect to the last `horizon` cached prefix rows
+ * of every window, from the chunk's queries only: the part of the exact reverse pass
+ * that a stop-gradient prefix drops ("train: walk the window", Why it's a draft: an
+ * exact reverse pass with horizon H = 0 ... all; "stop-gradient through context
+ * tokens", Mechanism: kept queries attend to the context's k/v, so context dK/dV
+ * are nonzero and feed the k/v weight gradients). With P_b the window's prefix:
+ *   dk_prefix[b][kv][h] = scale * sum_{g, i} dS[i][j] q[b][kv*G+g][i]
+ *   dv_prefix[b][kv][h] = sum_{g, i} P[i][j] d_o[b][kv*G+g][i],   j = P_b - H + h,
+ * with P and dS as in pka_chunk_attn_bwd, taken against the cache rows as the
+ * attention reads them (F16 / q8_0 dequantised to bf16); rows with j < 0 (P_b < H)
+ * are written as 0. Outputs are f32 [B][Hkv][H][D]. Inputs: the chunk's q and d_o,
+ * the forward's lse and the backward's delta (pka_chunk_attn_bwd with delta != NULL).
+ * 0 <= horizon <= prefix_len; horizon = 0 writes nothing. ws:
+ * pka_prefix_kv_grad_workspace_bytes(dims, horizon) bytes (may be NULL if 0). */
+size_t pka_prefix_kv_grad_workspace_bytes(const pka_dims* dims, int64_t horizon);
+pka_status pka_prefix_kv_grad(const pka_dims* dims, int64_t horizon, const void* q,
+                              const pka_cache* cache, const float* lse, const void* d_o,
+                              const float* delta, float* dk_prefix, float* dv_prefix,
+                              void* ws, size_t ws_bytes, pka_stream_t stream);
+
 /* Re-decode of the chunk into the cache ("train: walk the window", What it is and
  * Contents): writes cache rows [P, P+C) of every (window, KV head) from k, v
  * (bf16 [B][Hkv][C][D]). Uses batch, n_heads_kv, head_dim, prefix_len, chunk_len of
@@ -182,7 +202,9 @@ typedef enum {
   PKA_KERNEL_APPEND = 6,     /* kv_append_*                                        */
   PKA_KERNEL_DEQUANT = 7,    /* kv_dequant_q8_0                                    */
   PKA_KERNEL_BWD_DKDV_REDUCE = 8, /* reserved: folded into PKA_KERNEL_BWD_DQ_REDUCE */
-  PKA_KERNEL_COUNT = 9
+  PKA_KERNEL_PREFIX_KV = 9,  /* prefix dk, dv within the horizon                    */
+  PKA_KERNEL_PREFIX_KV_REDUCE = 10, /* sums of their row-split partials             */
+  PKA_KERNEL_COUNT = 11
 } pka_kernel_id;
 
 pka_status pka_profile_enable(int32_t on);

@@ -7,8 +7,8 @@ if the library is missing; there is no fallback implementation.
 
 Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
 ``chunk_attn_fwd``, ``chunk_attn_bwd``, ``kv_append_q8_0``, ``kv_append_f16``,
-``kv_append_bf16``, ``kv_dequant_q8_0``, ``fwd_workspace_bytes``,
-``bwd_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
+``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``, ``fwd_workspace_bytes``,
+``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
 constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
 chunk loop of a batch of windows: step, append, advance every window's prefix.
@@ -37,7 +37,8 @@ CACHE_TYPE_BY_NAME = {"f16": CACHE_F16, "bf16": CACHE_BF16, "q8_0": CACHE_Q8_0}
 STATUS = {0: "PKA_OK", 1: "PKA_ERR_NULL", 2: "PKA_ERR_DIMS", 3: "PKA_ERR_UNSUPPORTED",
           4: "PKA_ERR_CAPACITY", 5: "PKA_ERR_ALIGN", 6: "PKA_ERR_WORKSPACE", 7: "PKA_ERR_HIP"}
 KERNELS = {"fwd": 0, "fwd_combine": 1, "bwd_prep": 2, "bwd_dq": 3, "bwd_dkdv": 4,
-           "bwd_dq_reduce": 5, "append": 6, "dequant": 7, "bwd_dkdv_reduce": 8}
+           "bwd_dq_reduce": 5, "append": 6, "dequant": 7, "bwd_dkdv_reduce": 8,
+           "prefix_kv": 9, "prefix_kv_reduce": 10}
 
 
 class Dims(ctypes.Structure):
@@ -62,6 +63,9 @@ _SIGS = {
                                           _vp, _sz, _vp]),
     "pka_chunk_attn_bwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pka_prefix_kv_grad_workspace_bytes": (_sz, [_P(Dims), _i64]),
+    "pka_prefix_kv_grad": (ctypes.c_int, [_P(Dims), _i64, _vp, _P(CacheDesc), _vp, _vp, _vp,
+                                          _vp, _vp, _vp, _sz, _vp]),
     "pka_kv_append_q8_0": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
     "pka_kv_append_f16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
     "pka_kv_append_bf16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
@@ -207,6 +211,36 @@ def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o
                                    0 if ws is None else ws.numel(), _stream(q.device)),
            "pka_chunk_attn_bwd")
     return dq, dk, dv
+
+
+def prefix_kv_grad_workspace_bytes(dims: Dims, horizon: int) -> int:
+    return int(_lib.pka_prefix_kv_grad_workspace_bytes(ctypes.byref(dims), int(horizon)))
+
+
+def prefix_kv_grad(q, cache: PrefixCache, prefix_len: int, scale: float, lse, d_o, delta,
+                   horizon: int, dk=None, dv=None, ws=None, prefix_lens=None):
+    """dK, dV (f32 [B][Hkv][H][D]) of the last `horizon` cache rows of every window from
+    the chunk queries; row h is cache row P_b - H + h (zero where P_b < H). lse is the
+    forward's, delta the backward's (chunk_attn_bwd(..., delta=...))."""
+    _need(q, "q")
+    _need(d_o, "d_o")
+    _need(lse, "lse", torch.float32)
+    _need(delta, "delta", torch.float32)
+    B, Hq, C, D = q.shape
+    Hkv = cache.n_heads_kv
+    dims = make_dims(B, Hq, Hkv, D, prefix_len, C, scale, prefix_lens)
+    shape = (B, Hkv, int(horizon), D)
+    dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
+    dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    if ws is None:
+        ws = _workspace(prefix_kv_grad_workspace_bytes(dims, horizon), q.device)
+    cd = cache.desc()
+    _check(_lib.pka_prefix_kv_grad(ctypes.byref(dims), int(horizon), _ptr(q), ctypes.byref(cd),
+                                   _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dk), _ptr(dv),
+                                   _ptr(ws), 0 if ws is None else ws.numel(),
+                                   _stream(q.device)),
+           "pka_prefix_kv_grad")
+    return dk, dv
 
 
 def _append(fn, name, k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):

@@ -226,8 +226,15 @@ struct DkvLds {
   __align__(16) int tok[2][BQ];
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
+// dK/dV of one block of 64 keys of one (window, KV head), over the packed query
+// rows of all G heads that see them. PREFIX = false: the chunk's own keys (causal:
+// rows whose token is >= the key), bf16 outputs dk, dv [B][Hkv][C][D].
+// PREFIX = true: the last `horizon` cache rows [P_b - H, P_b) of the window (every
+// chunk row sees them), dequantised on load like the forward; fp32 outputs
+// dkp, dvp [B][Hkv][H][D] whose row h is cache row P_b - H + h (zero when that row
+// does not exist because P_b < H).
+template <int D, int CT, bool PREFIX>
+__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   __shared__ __align__(16) DkvLds<D> sm;
   constexpr int S = DkvLds<D>::S;
   constexpr int NKS = D / 16;
@@ -244,7 +251,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int C = (int)p.C;
   const int G = p.G;
   const int rows = G * C;
-  const int nkb = (C + KB - 1) / KB;
+  const int NK = PREFIX ? (int)p.horizon : C;   // keys of this launch per (b, kv)
+  const int nkb = (NK + KB - 1) / KB;
   const int RS = p.plan.n_dkv_split;
   const int L = blockIdx.x;
   const int rsplit = L % RS;
@@ -253,10 +261,32 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
 
-  const int key = kblk * KB + kw * 32 + l32;  // chunk index
-  const bool key_ok = key < C;
+  const int key = kblk * KB + kw * 32 + l32;  // key index of this launch
+  bool key_ok = key < NK;
   bf16x8 kreg[NKS], vreg[NKS];
-  {
+  if constexpr (PREFIX) {
+    const int64_t Pb = window_prefix(p.plens, b, p.P);
+    const int64_t j = Pb - NK + key;           // cache row
+    key_ok = key_ok && j >= 0;
+    constexpr int ESZ = (CT == kQ8) ? 1 : 2;
+    const char* ck = static_cast<const char*>(p.cache.k) + bh * p.cache.cap * D * ESZ;
+    const char* cv = static_cast<const char*>(p.cache.v) + bh * p.cache.cap * D * ESZ;
+    const uint16_t* cks = (CT == kQ8) ? p.cache.ks + bh * p.cache.cap * (D / 32) : nullptr;
+    const uint16_t* cvs = (CT == kQ8) ? p.cache.vs + bh * p.cache.cap * (D / 32) : nullptr;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (key_ok) {
+        RawRow8 rk, rv;
+        load_row8<CT, D>(rk, ck, cks, nullptr, Pb, 0, j, ks * 16 + hf * 8);
+        load_row8<CT, D>(rv, cv, cvs, nullptr, Pb, 0, j, ks * 16 + hf * 8);
+        kreg[ks] = __builtin_bit_cast(bf16x8, to_bf16x8<CT>(rk, true));
+        vreg[ks] = __builtin_bit_cast(bf16x8, to_bf16x8<CT>(rv, true));
+      } else {
+        kreg[ks] = bf16x8{};
+        vreg[ks] = bf16x8{};
+      }
+    }
+  } else {
     const uint16_t* kp = p.kc + (bh * C + (key_ok ? key : 0)) * D + hf * 8;
     const uint16_t* vp = p.vc + (bh * C + (key_ok ? key : 0)) * D + hf * 8;
 #pragma unroll
@@ -278,7 +308,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
   const float c = p.scale_log2;
 
   // Rows whose token is >= the block's first key can see some key of it.
-  const int r_unit = kblk * KB * G;
+  const int r_unit = PREFIX ? 0 : kblk * KB * G;
   const int steps_unit = (rows - r_unit + BQ - 1) / BQ;
   const int s_lo = (int)((int64_t)rsplit * steps_unit / RS);
   const int s_hi = (int)((int64_t)(rsplit + 1) * steps_unit / RS);
@@ -393,7 +423,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       for (int j = 0; j < 4; ++j) {
         const int i = g4 * 4 + j;
         const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l4[j]));
-        const float pv = key <= tk[j] ? e : 0.f;
+        const float pv = (PREFIX ? tk[j] >= 0 : key <= tk[j]) ? e : 0.f;
         pb[i >> 3][i & 7] = (__bf16)pv;
         dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - d4[j]));
       }
@@ -424,19 +454,38 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
       }
   }
   __syncthreads();
-  if (qb == 1 || !key_ok) return;
+  if (qb == 1 || key >= NK) return;
+  // A prefix row that does not exist (P_b < H) gets an exact zero.
+  const float keep = key_ok ? 1.f : 0.f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acck[db][i] += red[(db * 16 + i) * 64 + lane];
-      accv[db][i] += red[32 * D + (db * 16 + i) * 64 + lane];
+      acck[db][i] = (acck[db][i] + red[(db * 16 + i) * 64 + lane]) * keep;
+      accv[db][i] = (accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane]) * keep;
     }
   const float sc = p.scale;
+  if (PREFIX && RS == 1) {
+    float* pk = p.dkp + (bh * NK + key) * D;
+    float* pv = p.dvp + (bh * NK + key) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hf * 4;
+        *reinterpret_cast<f32x4*>(pk + d) =
+            f32x4{acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc,
+                  acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc};
+        *reinterpret_cast<f32x4*>(pv + d) =
+            f32x4{accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1], accv[db][g4 * 4 + 2],
+                  accv[db][g4 * 4 + 3]};
+      }
+    return;
+  }
   if (RS > 1) {
     // fp32 partials of this row split, summed in split order by bwd_reduce.
-    const int64_t nkey = (int64_t)p.B * p.Hkv * C;
-    float* pk = p.ws_dkv + ((int64_t)rsplit * 2 * nkey + bh * C + key) * D;
+    const int64_t nkey = (int64_t)p.B * p.Hkv * NK;
+    float* pk = p.ws_dkv + ((int64_t)rsplit * 2 * nkey + bh * NK + key) * D;
     float* pv = pk + nkey * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -472,15 +521,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdParams p) {
 // Sums of split partials, in split order, written as bf16 (one launch for both):
 // threads [0, n_dq) reduce dQ rows (prefix split of the dQ kernel), the rest reduce
 // dK and dV rows (query-row split of the dK/dV kernel).
-template <int D>
+template <int D, bool F32OUT>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_dq,
-                                                         int64_t n_dkv) {
+                                                         int64_t n_dkv, int64_t nk) {
   constexpr int CH = D / 8;
   int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const float* src;
   int64_t stride;  // floats between consecutive splits
   int nsplit;
-  uint16_t* dst;
+  uint16_t* dst = nullptr;
+  float* dst32 = nullptr;
   if (idx < n_dq) {
     const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
     const int64_t row = idx / CH;
@@ -492,7 +542,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_
   } else {
     idx -= n_dq;
     if (idx >= n_dkv) return;   // n_dkv is 0 when dK/dV rows were not split
-    const int64_t nkey = (int64_t)p.B * p.Hkv * p.C;
+    const int64_t nkey = (int64_t)p.B * p.Hkv * nk;
     const int which = (int)(idx / (nkey * CH));   // 0: dK, 1: dV
     const int64_t rem = idx - which * nkey * CH;
     const int64_t row = rem / CH;
@@ -500,7 +550,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_
     src = p.ws_dkv + (which * nkey + row) * D + c8 * 8;
     stride = 2 * nkey * D;
     nsplit = p.plan.n_dkv_split;
-    dst = (which ? p.dv : p.dk) + row * D + c8 * 8;
+    if (F32OUT)
+      dst32 = (which ? p.dvp : p.dkp) + row * D + c8 * 8;
+    else
+      dst = (which ? p.dv : p.dk) + row * D + c8 * 8;
   }
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < nsplit; ++s) {
@@ -512,8 +565,13 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_
       o[4 + i] += bq[i];
     }
   }
-  *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
-                                         pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
+  if (F32OUT) {
+    reinterpret_cast<f32x4*>(dst32)[0] = f32x4{o[0], o[1], o[2], o[3]};
+    reinterpret_cast<f32x4*>(dst32)[1] = f32x4{o[4], o[5], o[6], o[7]};
+  } else {
+    *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]),
+                                           pack_bf16(o[4], o[5]), pack_bf16(o[6], o[7])};
+  }
 }
 
 template <int D, int CT>
@@ -527,8 +585,8 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
 
   const int nkb = (int)((p.C + KB - 1) / KB);
   prof_begin(PKA_KERNEL_BWD_DKDV, s);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split),
-                     dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kBF16, false>),
+                     dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split), dim3(256), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DKDV, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -536,15 +594,44 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   const int64_t n_dkv = p.plan.n_dkv_split > 1 ? 2 * (int64_t)p.B * p.Hkv * p.C * (D / 8) : 0;
   if (n_dq + n_dkv > 0) {
     prof_begin(PKA_KERNEL_BWD_DQ_REDUCE, s);
-    hipLaunchKernelGGL((bwd_reduce_kernel<D>), dim3((unsigned)((n_dq + n_dkv + 255) / 256)),
-                       dim3(256), 0, s, p, n_dq, n_dkv);
+    hipLaunchKernelGGL((bwd_reduce_kernel<D, false>),
+                       dim3((unsigned)((n_dq + n_dkv + 255) / 256)), dim3(256), 0, s, p, n_dq,
+                       n_dkv, p.C);
     prof_end(PKA_KERNEL_BWD_DQ_REDUCE, s);
     e = hipGetLastError();
   }
   return e;
 }
 
+template <int D, int CT>
+hipError_t launch_prefix_kv_t(const BwdParams& p, hipStream_t s) {
+  hipError_t e;
+  const int nkb = (int)((p.horizon + KB - 1) / KB);
+  prof_begin(PKA_KERNEL_PREFIX_KV, s);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, CT, true>),
+                     dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split), dim3(256), 0, s, p);
+  prof_end(PKA_KERNEL_PREFIX_KV, s);
+  if ((e = hipGetLastError()) != hipSuccess || p.plan.n_dkv_split == 1) return e;
+  const int64_t n_dkv = 2 * (int64_t)p.B * p.Hkv * p.horizon * (D / 8);
+  prof_begin(PKA_KERNEL_PREFIX_KV_REDUCE, s);
+  hipLaunchKernelGGL((bwd_reduce_kernel<D, true>), dim3((unsigned)((n_dkv + 255) / 256)),
+                     dim3(256), 0, s, p, (int64_t)0, n_dkv, p.horizon);
+  prof_end(PKA_KERNEL_PREFIX_KV_REDUCE, s);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_prefix_kv(const BwdParams& p, int D, int cache_type, hipStream_t s) {
+  if (D == 128) {
+    if (cache_type == kF16) return launch_prefix_kv_t<128, kF16>(p, s);
+    if (cache_type == kBF16) return launch_prefix_kv_t<128, kBF16>(p, s);
+    return launch_prefix_kv_t<128, kQ8>(p, s);
+  }
+  if (cache_type == kF16) return launch_prefix_kv_t<64, kF16>(p, s);
+  if (cache_type == kBF16) return launch_prefix_kv_t<64, kBF16>(p, s);
+  return launch_prefix_kv_t<64, kQ8>(p, s);
+}
 
 hipError_t launch_bwd(const BwdParams& p, int D, int cache_type, hipStream_t s) {
   if (D == 128) {

@@ -193,6 +193,28 @@ Plan plan_bwd(const pka_dims& d) {
   return pl;
 }
 
+// Prefix gradient: one unit per (window, KV head, block of 64 prefix keys of the
+// horizon), split over query rows like the chunk dK/dV when units are few.
+Plan plan_prefix_kv(const pka_dims& d, int64_t horizon) {
+  Plan pl{};
+  pl.n_rb = 0;
+  pl.n_split = 1;
+  pl.nblk = 0;
+  const int64_t G = d.n_heads_q / d.n_heads_kv;
+  const int64_t nkb = (horizon + kDkvKeysPerBlock - 1) / kDkvKeysPerBlock;
+  const int64_t units = (int64_t)d.batch * d.n_heads_kv * nkb;
+  int64_t split = 1;
+  if (units > 0 && units < kNumCUs) {
+    split = kNumCUs / units;
+    const int64_t max_steps = (G * d.chunk_len + 63) / 64;
+    const int64_t max_split = max_steps / 2 > 1 ? max_steps / 2 : 1;
+    if (split > max_split) split = max_split;
+    if (split > 16) split = 16;
+  }
+  pl.n_dkv_split = (int)split;
+  return pl;
+}
+
 }  // namespace pka
 
 using namespace pka;
@@ -328,6 +350,69 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
   if (p.plan.n_dkv_split > 1) p.ws_dkv = reinterpret_cast<float*>(static_cast<char*>(ws) + off);
   hipError_t e = launch_bwd(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "chunk_attn_bwd launch");
+  return PKA_OK;
+}
+
+static pka_status check_horizon(const pka_dims* dims, int64_t horizon) {
+  if (horizon < 0 || horizon > dims->prefix_len)
+    return fail(PKA_ERR_DIMS, "horizon %lld outside [0, prefix_len = %lld]", (long long)horizon,
+                (long long)dims->prefix_len);
+  if ((int64_t)dims->batch * dims->n_heads_kv * horizon > kMaxSeq)
+    return fail(PKA_ERR_DIMS, "batch * n_heads_kv * horizon exceeds 2^31 - 1");
+  return PKA_OK;
+}
+
+size_t pka_prefix_kv_grad_workspace_bytes(const pka_dims* dims, int64_t horizon) {
+  if (check_dims(dims) != PKA_OK || check_horizon(dims, horizon) != PKA_OK) return 0;
+  const Plan pl = plan_prefix_kv(*dims, horizon);
+  if (pl.n_dkv_split <= 1) return 0;
+  return align256((size_t)pl.n_dkv_split * 2 * dims->batch * dims->n_heads_kv * horizon *
+                  dims->head_dim * 4);
+}
+
+pka_status pka_prefix_kv_grad(const pka_dims* dims, int64_t horizon, const void* q,
+                              const pka_cache* cache, const float* lse, const void* d_o,
+                              const float* delta, float* dk_prefix, float* dv_prefix,
+                              void* ws, size_t ws_bytes, pka_stream_t stream) {
+  g_last_error[0] = 0;
+  pka_status st;
+  if ((st = check_dims(dims)) != PKA_OK) return st;
+  if ((st = check_horizon(dims, horizon)) != PKA_OK) return st;
+  if ((st = check_ptrs({q, lse, d_o, delta, dk_prefix, dv_prefix},
+                       "q, lse, d_o, delta, dk_prefix, dv_prefix")) != PKA_OK)
+    return st;
+  if ((st = check_cache(cache, dims, dims->prefix_len, false)) != PKA_OK) return st;
+  const size_t need = pka_prefix_kv_grad_workspace_bytes(dims, horizon);
+  if (need > 0) {
+    if (!ws || ws_bytes < need)
+      return fail(PKA_ERR_WORKSPACE, "prefix gradient needs %zu workspace bytes, got %zu", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(PKA_ERR_ALIGN, "workspace not 16-byte aligned");
+  }
+  if (horizon == 0) return PKA_OK;   // nothing to write
+  BwdParams p{};
+  p.q = static_cast<const uint16_t*>(q);
+  p.cache = cache_ref(cache);
+  p.lse = lse;
+  p.d_o = static_cast<const uint16_t*>(d_o);
+  p.delta = const_cast<float*>(delta);
+  p.dkp = dk_prefix;
+  p.dvp = dv_prefix;
+  p.horizon = horizon;
+  p.B = dims->batch;
+  p.Hq = dims->n_heads_q;
+  p.Hkv = dims->n_heads_kv;
+  p.G = dims->n_heads_q / dims->n_heads_kv;
+  p.P = dims->prefix_len;
+  p.plens = dims->prefix_lens;
+  p.C = dims->chunk_len;
+  p.scale = dims->softmax_scale;
+  p.scale_log2 = (float)((double)dims->softmax_scale * 1.4426950408889634);
+  p.plan = plan_prefix_kv(*dims, horizon);
+  if (p.plan.n_dkv_split > 1) p.ws_dkv = static_cast<float*>(ws);
+  hipError_t e =
+      launch_prefix_kv(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefix_kv_grad launch");
   return PKA_OK;
 }
 

@@ -67,7 +67,10 @@ struct BwdParams {
   uint16_t* dv;
   float* delta;   // [B*Hq*C]: caller's buffer or workspace
   float* ws_dq;   // [n_split][B*Hq*C][D] (only when n_split > 1)
-  float* ws_dkv;  // [n_dkv_split][2][B*Hkv*C][D] (only when n_dkv_split > 1)
+  float* ws_dkv;  // [n_dkv_split][2][B*Hkv*NK][D] (only when n_dkv_split > 1)
+  int64_t horizon;  // prefix gradient: the last `horizon` cache rows of each window
+  float* dkp;       // prefix gradient outputs f32 [B][Hkv][horizon][D]
+  float* dvp;
   int B, Hq, Hkv, G;
   int64_t P, C;
   const int32_t* plens;
@@ -104,6 +107,7 @@ struct DequantParams {
 
 Plan plan_fwd(const pka_dims& d);
 Plan plan_bwd(const pka_dims& d);
+Plan plan_prefix_kv(const pka_dims& d, int64_t horizon);
 
 // Profiling brackets (no-ops unless enabled).
 void prof_begin(int kernel, hipStream_t s);
@@ -111,6 +115,7 @@ void prof_end(int kernel, hipStream_t s);
 
 hipError_t launch_fwd(const FwdParams& p, int D, int cache_type, hipStream_t s);
 hipError_t launch_bwd(const BwdParams& p, int D, int cache_type, hipStream_t s);
+hipError_t launch_prefix_kv(const BwdParams& p, int D, int cache_type, hipStream_t s);
 hipError_t launch_append(const AppendParams& p, int cache_type, hipStream_t s);
 hipError_t launch_dequant(const DequantParams& p, hipStream_t s);
 

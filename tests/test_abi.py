@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("pka_chunk_attn_fwd", "pka_chunk_attn_bwd", "pka_kv_append_q8_0",
               "pka_kv_append_f16", "pka_kv_append_bf16", "pka_kv_dequant_q8_0",
-              "pka_fwd_workspace_bytes", "pka_bwd_workspace_bytes", "pka_status_string",
+              "pka_fwd_workspace_bytes", "pka_bwd_workspace_bytes", "pka_prefix_kv_grad",
+              "pka_prefix_kv_grad_workspace_bytes", "pka_status_string",
               "pka_last_error", "pka_profile_enable", "pka_profile_reset", "pka_profile_read"):
         assert n in names
 
@@ -221,3 +222,33 @@ def test_prefix_lens_alignment_is_checked(pka):
     assert st == 5 and "prefix_lens" in msg
     c = cache(pka, capacity=600, type=pka.CACHE_F16)
     assert pka.lib.pka_kv_append_f16(ctypes.byref(d), A, A, ctypes.byref(c), None) == 5
+
+
+def test_prefix_kv_grad_validation(pka):
+    lib = pka.lib
+    d = dims(pka)                                    # P = 256
+    c = cache(pka)
+
+    def call(horizon, ptrs=None, ws=None, ws_bytes=0, dd=d, cc=c):
+        p = dict(q=A, lse=A, do=A, delta=A, dk=A, dv=A)
+        p.update(ptrs or {})
+        st = lib.pka_prefix_kv_grad(ctypes.byref(dd), horizon, p["q"], ctypes.byref(cc),
+                                    p["lse"], p["do"], p["delta"], p["dk"], p["dv"], ws,
+                                    ws_bytes, None)
+        return st, lib.pka_last_error().decode()
+
+    assert call(257)[0] == 2 and call(-1)[0] == 2          # horizon outside [0, P]
+    assert call(64, {"delta": None})[0] == 1
+    assert call(64, {"dk": MIS})[0] == 5
+    assert call(64, cc=cache(pka, capacity=100))[0] == 4
+    assert call(64, dd=dims(pka, n_heads_kv=3))[0] == 2
+    # few units and many query rows -> row splits with an fp32 partial workspace
+    dl = dims(pka, chunk_len=1024)
+    need = pka.prefix_kv_grad_workspace_bytes(dl, 64)
+    assert need >= 2 * 1 * 2 * 64 * 128 * 4 and need % 256 == 0
+    st, msg = call(64, dd=dl)
+    assert st == 6 and "workspace" in msg
+    assert call(64, ws=MIS, ws_bytes=need, dd=dl)[0] == 5
+    # horizon 0 is valid and writes nothing (no launch, so fake pointers are fine)
+    assert call(0)[0] == 0
+    assert pka.prefix_kv_grad_workspace_bytes(d, 300) == 0     # invalid -> 0
