@@ -123,6 +123,46 @@ def cpu_baseline(w, inputs, budget_s=15.0):
                       f"keys each), fp64 forward + backward, {spent:.1f} s"}
 
 
+def time_prefix_kv_grad(pka, w, t, cache, horizon, steps, warmup):
+    """Time pka_prefix_kv_grad (dK/dV of the last H prefix rows from the chunk queries)
+    over `steps` launches with HIP events around each launch. Work: 4 contractions (S
+    and dP recomputed, dK, dV) of 2*D FLOP per (chunk query, horizon key) pair."""
+    import torch
+    P, sc = w.prefix_len, w.softmax_scale
+    H = min(int(horizon), P)
+    q, kc, vc, o, lse, do = t["q"], t["kc"], t["vc"], t["o"], t["lse"], t["do"]
+    delta = torch.empty(lse.shape, dtype=torch.float32, device=q.device)
+    pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=o, lse=lse)
+    pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, delta=delta)
+    shape = (w.batch, w.n_heads_kv, H, w.head_dim)
+    dkp = torch.empty(shape, dtype=torch.float32, device=q.device)
+    dvp = torch.empty(shape, dtype=torch.float32, device=q.device)
+    dims = pka.make_dims(w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, P, w.chunk_len, sc)
+    nws = pka.prefix_kv_grad_workspace_bytes(dims, H)
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+
+    def run():
+        pka.prefix_kv_grad(q, cache, P, sc, lse, do, delta, H, dk=dkp, dv=dvp, ws=ws)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    pka.profile_reset()
+    pka.profile_enable(True)
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    pka.profile_enable(False)
+    tot, n, _ = pka.profile_read("prefix_kv")
+    ms = tot / n
+    red_tot, red_n, _ = pka.profile_read("prefix_kv_reduce")
+    flop = 4 * 2 * w.head_dim * w.batch * w.n_heads_q * w.chunk_len * H
+    return {"horizon": H, "kernel_ms": round(ms, 5),
+            "reduce_ms": round(red_tot / red_n, 5) if red_n else 0.0,
+            "flop_per_launch": flop, "achieved": round(flop / (ms * 1e-3) / 1e12, 2),
+            "unit": "TFLOP/s", "frac": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +173,9 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the step without the per-kernel HIP events")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--prefix-horizon", type=int, default=0,
+                    help="also time pka_prefix_kv_grad (dK/dV of the last H prefix rows) "
+                         "on the same inputs, outside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM "
                          "byte counters of a profiler run)")
@@ -233,6 +276,10 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.prefix_horizon > 0:
+        out["prefix_kv_grad"] = time_prefix_kv_grad(
+            pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
+            args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
     print(json.dumps(out), flush=True)
