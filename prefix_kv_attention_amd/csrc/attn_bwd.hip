@@ -222,7 +222,7 @@ struct DkvLds {
     float red[2][32 * D * 2];  // partial dK^T, dV^T of waves 2-3 (fp32)
   } u;
   __align__(16) float lse2[2][BQ];
-  __align__(16) float dlt[2][BQ];
+  __align__(16) float dlt[2][BQ];   // -delta of the staged rows
   __align__(16) int tok[2][BQ];
 };
 
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
       if (r0 + tid < rows) {
         const int64_t row = (head0 + gl) * C + tl;
         pl = p.lse[row] * kLog2e;
-        pd = p.delta[row];
+        pd = -p.delta[row];   // staged negated: the dP^T chain starts from it
         ptok = tl;
       } else {
         pl = 0.f;
@@ -399,11 +399,22 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     if (n_steps > 1) issue(1);
     __syncthreads();
   }
+  // Packed rows from clean_from on have tokens >= the block's last key: no mask.
+  const int clean_from = (kblk * KB + KB - 1) * G;
   for (int step = 0; step < n_steps; ++step) {
     const int cur = step & 1;
     const uint16_t* qt = sm.u.t.q[cur];
     const uint16_t* gt = sm.u.t.g[cur];
-    f32x16 s = f32x16{}, dp = f32x16{};
+    const bool diag = !PREFIX && r_begin + step * BQ < clean_from;
+    // dP (rows x keys) starts from -delta of its rows, so the chain yields dP - delta;
+    // register i of the result is row (i / 4) * 8 + hf * 4 + i % 4 of the wave's 32.
+    f32x16 s = f32x16{}, dp;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qb * 32 + g4 * 8 + hf * 4]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dp[g4 * 4 + j] = d4[j];
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       s = mfma32(*reinterpret_cast<const bf16x8*>(&qt[a_off + ks * 16]), kreg[ks], s);
@@ -416,16 +427,18 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
       // read per per-row array
       const int q0 = qb * 32 + g4 * 8 + hf * 4;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][q0]);
       const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
       const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = g4 * 4 + j;
         const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l4[j]));
-        const float pv = (PREFIX ? tk[j] >= 0 : key <= tk[j]) ? e : 0.f;
+        // Prefix keys are seen by every row; padding rows past the last one have
+        // zero q and dO and so add nothing. Chunk keys: causal, checked only in the
+        // steps that reach below the block's last key.
+        const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
         pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * (dp[i] - d4[j]));
+        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
       }
     }
 #pragma unroll
@@ -456,13 +469,12 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   __syncthreads();
   if (qb == 1 || key >= NK) return;
   // A prefix row that does not exist (P_b < H) gets an exact zero.
-  const float keep = key_ok ? 1.f : 0.f;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acck[db][i] = (acck[db][i] + red[(db * 16 + i) * 64 + lane]) * keep;
-      accv[db][i] = (accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane]) * keep;
+      acck[db][i] = key_ok ? acck[db][i] + red[(db * 16 + i) * 64 + lane] : 0.f;
+      accv[db][i] = key_ok ? accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane] : 0.f;
     }
   const float sc = p.scale;
   if (PREFIX && RS == 1) {
