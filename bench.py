@@ -163,6 +163,35 @@ def time_prefix_kv_grad(pka, w, t, cache, horizon, steps, warmup):
             "unit": "TFLOP/s", "frac": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def time_decode(pka, w, t, cache, steps, warmup):
+    """Time the re-decode of a chunk into the cache two ways: one fused launch
+    (pka_chunk_attn_fwd_append) against pka_chunk_attn_fwd followed by
+    pka_kv_append_*. Both write the same O, LSE and cache rows [P, P + C); wall time
+    per call over `steps` calls, synchronised on both sides."""
+    import torch
+    P, sc = w.prefix_len, w.softmax_scale
+    q, kc, vc, o, lse = t["q"], t["kc"], t["vc"], t["o"], t["lse"]
+
+    def fused():
+        pka.chunk_attn_fwd_append(q, kc, vc, cache, P, sc, o=o, lse=lse)
+
+    def separate():
+        pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=o, lse=lse)
+        pka.kv_append(kc, vc, cache, P)
+
+    res = {}
+    for name, fn in (("separate_ms", separate), ("fused_ms", fused)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        res[name] = round((time.perf_counter() - t0) * 1e3 / steps, 5)
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +205,9 @@ def main():
     ap.add_argument("--prefix-horizon", type=int, default=0,
                     help="also time pka_prefix_kv_grad (dK/dV of the last H prefix rows) "
                          "on the same inputs, outside the step")
+    ap.add_argument("--decode", action="store_true",
+                    help="also time the fused forward + cache append against the two "
+                         "separate calls, outside the step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM "
                          "byte counters of a profiler run)")
@@ -280,6 +312,9 @@ def main():
         out["prefix_kv_grad"] = time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
             args.steps, args.warmup)
+    if args.decode:
+        out["decode"] = time_decode(pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse), cache,
+                                    args.steps, args.warmup)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -122,6 +122,20 @@ pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k
                               float* lse, void* ws, size_t ws_bytes,
                               pka_stream_t stream);
 
+/* The forward above fused with the re-decode of the chunk into the cache: one launch
+ * computes o and lse exactly as pka_chunk_attn_fwd (the chunk's own keys are the
+ * bf16 k, v) and writes rows [P_b, P_b + C) of the cache from k, v exactly as the
+ * pka_kv_append_* call of the cache's type would. This is the no-grad forward of a
+ * context piece that builds the cache chunk by chunk ("Context-Frozen Training", The
+ * Solution, Phase 1: a forward without gradients fills the KV cache; "train: walk the
+ * window", What it is: the chunk is re-decoded into the cache so the next one sees
+ * it). Requires prefix_len + C <= capacity. The rows written are never read by the
+ * same launch, so the fusion changes no value. */
+pka_status pka_chunk_attn_fwd_append(const pka_dims* dims, const void* q, const void* k,
+                                     const void* v, const pka_cache* cache, void* o,
+                                     float* lse, void* ws, size_t ws_bytes,
+                                     pka_stream_t stream);
+
 /* Backward of the forward above from the upstream gradient d_o on the chunk rows.
  * Computes delta = rowsum(d_o * o), then
  *   dq = scale * dS K      over prefix and chunk keys,

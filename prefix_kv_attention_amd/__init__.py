@@ -6,7 +6,7 @@ provides device memory and the current HIP stream. Importing this package raises
 if the library is missing; there is no fallback implementation.
 
 Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
-``chunk_attn_fwd``, ``chunk_attn_bwd``, ``kv_append_q8_0``, ``kv_append_f16``,
+``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``, ``kv_append_f16``,
 ``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``, ``fwd_workspace_bytes``,
 ``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
@@ -61,6 +61,8 @@ _SIGS = {
     "pka_bwd_workspace_bytes": (_sz, [_P(Dims)]),
     "pka_chunk_attn_fwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
                                           _vp, _sz, _vp]),
+    "pka_chunk_attn_fwd_append": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp,
+                                                 _vp, _vp, _sz, _vp]),
     "pka_chunk_attn_bwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pka_prefix_kv_grad_workspace_bytes": (_sz, [_P(Dims), _i64]),
@@ -189,6 +191,26 @@ def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
                                    ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws),
                                    0 if ws is None else ws.numel(), _stream(q.device)),
            "pka_chunk_attn_fwd")
+    return o, lse
+
+
+def chunk_attn_fwd_append(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
+                          o=None, lse=None, ws=None, prefix_lens=None):
+    """chunk_attn_fwd and the append of k, v to cache rows [P_b, P_b + C) in one launch."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = _workspace(fwd_workspace_bytes(dims), q.device)
+    cd = cache.desc()
+    _check(_lib.pka_chunk_attn_fwd_append(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                          ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(q.device)),
+           "pka_chunk_attn_fwd_append")
     return o, lse
 
 
@@ -350,6 +372,19 @@ class WindowWalk:
         kv_append(k, v, self.cache, self.prefix_len, prefix_lens=self._plens())
         self.lens = [p + C for p in self.lens]
         self._dev += C
+
+    def decode(self, q, k, v):
+        """No-grad forward of one chunk fused with its append (the pass that builds the
+        cache): (o, lse); then P_b += C."""
+        C = k.shape[2]
+        if self.prefix_len + C > self.cache.capacity:
+            raise ValueError(f"cache capacity {self.cache.capacity} < "
+                             f"{self.prefix_len + C} rows")
+        o, lse = chunk_attn_fwd_append(q, k, v, self.cache, self.prefix_len, self.scale,
+                                       prefix_lens=self._plens())
+        self.lens = [p + C for p in self.lens]
+        self._dev += C
+        return o, lse
 
     def step(self, q, k, v, d_o):
         """Forward, backward and append of one chunk: (o, lse, dq, dk, dv)."""

@@ -208,6 +208,18 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
     }
   }
 
+  // Fused re-decode: the workgroups of this (window, KV head) share the append of
+  // its chunk rows to cache rows [P_b, P_b + C). Those rows are never read by this
+  // launch (the chunk's keys come from kc / vc), so the writes race with nothing.
+  if (p.append) {
+    const int nu = n_rb * SPL, u = split * n_rb + rb;
+    const int64_t total = append_items<CT, D>(C);
+    const int64_t crow0 = bh * p.cache.cap + P;
+    for (int64_t it = (int64_t)u * NTHR + tid; it < total; it += (int64_t)nu * NTHR)
+      append_item<CT, D>(it, C, p.kc + bh * C * D, p.vc + bh * C * D, p.wk, p.wv, p.wks,
+                         p.wvs, crow0);
+  }
+
   const float l_tot = pair_sum(l);
   if (!row_ok) return;
   if (SPL == 1) {

@@ -5,92 +5,26 @@
 // holds F16 or q8_0 constants (same page, Contents) and V is cached untransposed so
 // it can be quantised along head_dim (approval comment). bf16 caches are a copy.
 //
-// q8_0 block (32 consecutive values of one token row along head_dim):
-//   amax = max|x|; d = amax / 127 (IEEE fp32 division; this library is built without
-//   fast-math, so '/' is correctly rounded); scale = fp16(d) (RNE);
-//   code = clamp(round_half_away_from_zero(x / d), -127, 127) using the fp32 d;
-//   amax == 0 stores scale 0 and codes 0. Dequantised value = f32(scale) * code,
-//   exact in fp32.
+// The q8_0 block format and the conversions are in pka_device.hpp (q8_0_block,
+// to_cache16); the fused forward + append of attn_fwd.hip uses the same functions.
 // These kernels move a few MiB and are bound by HBM latency and launch overhead.
 #include "pka_device.hpp"
 
 namespace pka {
 namespace {
 
-// One thread per 32-value block; K blocks first, then V blocks.
-template <int D>
-__global__ __launch_bounds__(256) void append_q8_0_kernel(AppendParams p) {
-  constexpr int NB = D / 32;
-  const int64_t nblk = p.rows * NB;
+// One thread per append item (a q8_0 block of 32 values, or 8 values for F16 /
+// BF16) of all (window, KV head) units.
+template <int CT, int D>
+__global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
+  const int64_t per_unit = append_items<CT, D>(p.C);
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 2 * nblk) return;
-  const bool is_v = idx >= nblk;
-  const int64_t i = is_v ? idx - nblk : idx;
-  const int64_t row = i / NB;           // (b*Hkv + kv) * C + t
-  const int blk = (int)(i % NB);
-  const int64_t bh = row / p.C, tok = row % p.C;
-  const uint16_t* src = (is_v ? p.v : p.k) + row * D + blk * 32;
-
-  float x[32];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const u32x4 w = reinterpret_cast<const u32x4*>(src)[c];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[c * 8 + 2 * e] = bf16_to_f32(w[e] & 0xffffu);
-      x[c * 8 + 2 * e + 1] = bf16_to_f32(w[e] >> 16);
-    }
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
-  const float d = amax / 127.0f;
-  u32x4 q[2];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      int code = 0;
-      if (d != 0.f) {
-        const float r = roundf(x[c * 4 + e] / d);  // halves away from zero
-        code = (int)fminf(fmaxf(r, -127.f), 127.f);
-      }
-      w |= (uint32_t)(code & 0xff) << (8 * e);
-    }
-    q[c >> 2][c & 3] = w;
-  }
-  const int64_t crow = bh * p.cap + window_prefix(p.plens, (int)(bh / p.Hkv), p.P) + tok;
-  int8_t* dst = static_cast<int8_t*>(is_v ? p.cv : p.ck) + crow * D + blk * 32;
-  reinterpret_cast<u32x4*>(dst)[0] = q[0];
-  reinterpret_cast<u32x4*>(dst)[1] = q[1];
-  (is_v ? p.cvs : p.cks)[crow * NB + blk] = f32_to_f16_bits(d);
-}
-
-// One thread per 8 values; F16 converts (RNE), BF16 copies.
-template <int CT>
-__global__ __launch_bounds__(256) void append_16_kernel(AppendParams p) {
-  const int CHK = p.D / 8;
-  const int64_t n = p.rows * CHK;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= 2 * n) return;
-  const bool is_v = idx >= n;
-  const int64_t i = is_v ? idx - n : idx;
-  const int64_t row = i / CHK;
-  const int c8 = (int)(i % CHK);
-  const int64_t bh = row / p.C, tok = row % p.C;
-  const u32x4 w = *reinterpret_cast<const u32x4*>((is_v ? p.v : p.k) + row * p.D + c8 * 8);
-  u32x4 o;
-  if constexpr (CT == kF16) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      o[e] = (uint32_t)f32_to_f16_bits(bf16_to_f32(w[e] & 0xffffu)) |
-             ((uint32_t)f32_to_f16_bits(bf16_to_f32(w[e] >> 16)) << 16);
-  } else {
-    o = w;
-  }
-  const int64_t crow = bh * p.cap + window_prefix(p.plens, (int)(bh / p.Hkv), p.P) + tok;
-  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(is_v ? p.cv : p.ck) + crow * p.D + c8 * 8) = o;
+  const int64_t bh = idx / per_unit;
+  if (bh * p.C >= p.rows) return;           // rows = B * Hkv * C
+  const int64_t it = idx - bh * per_unit;
+  const int64_t crow0 = bh * p.cap + window_prefix(p.plens, (int)(bh / p.Hkv), p.P);
+  append_item<CT, D>(it, p.C, p.k + bh * p.C * D, p.v + bh * p.C * D, p.ck, p.cv, p.cks,
+                     p.cvs, crow0);
 }
 
 // One thread per 8 values of K or V rows [row0, row0 + rows).
@@ -127,22 +61,23 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(DequantParams p) {
 
 }  // namespace
 
+template <int CT, int D>
+void launch_append_t(const AppendParams& p, hipStream_t s) {
+  const int64_t threads = p.rows / p.C * append_items<CT, D>(p.C);
+  hipLaunchKernelGGL((append_kernel<CT, D>), dim3((unsigned)((threads + 255) / 256)), dim3(256),
+                     0, s, p);
+}
+
 hipError_t launch_append(const AppendParams& p, int cache_type, hipStream_t s) {
   prof_begin(PKA_KERNEL_APPEND, s);
-  if (cache_type == kQ8) {
-    const int64_t threads = 2 * p.rows * (p.D / 32);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (p.D == 128)
-      hipLaunchKernelGGL(append_q8_0_kernel<128>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(append_q8_0_kernel<64>, grid, dim3(256), 0, s, p);
+  if (p.D == 128) {
+    if (cache_type == kQ8) launch_append_t<kQ8, 128>(p, s);
+    else if (cache_type == kF16) launch_append_t<kF16, 128>(p, s);
+    else launch_append_t<kBF16, 128>(p, s);
   } else {
-    const int64_t threads = 2 * p.rows * (p.D / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    if (cache_type == kF16)
-      hipLaunchKernelGGL(append_16_kernel<kF16>, grid, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(append_16_kernel<kBF16>, grid, dim3(256), 0, s, p);
+    if (cache_type == kQ8) launch_append_t<kQ8, 64>(p, s);
+    else if (cache_type == kF16) launch_append_t<kF16, 64>(p, s);
+    else launch_append_t<kBF16, 64>(p, s);
   }
   prof_end(PKA_KERNEL_APPEND, s);
   return hipGetLastError();

@@ -258,14 +258,15 @@ size_t pka_bwd_workspace_bytes(const pka_dims* dims) {
   return bytes;
 }
 
-pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k,
-                              const void* v, const pka_cache* cache, void* o, float* lse,
-                              void* ws, size_t ws_bytes, pka_stream_t stream) {
+static pka_status fwd_common(const pka_dims* dims, const void* q, const void* k,
+                             const void* v, const pka_cache* cache, void* o, float* lse,
+                             void* ws, size_t ws_bytes, pka_stream_t stream, bool append) {
   g_last_error[0] = 0;
   pka_status st;
   if ((st = check_dims(dims)) != PKA_OK) return st;
   if ((st = check_ptrs({q, k, v, o, lse}, "q, k, v, o, lse")) != PKA_OK) return st;
-  if ((st = check_cache(cache, dims, dims->prefix_len, false)) != PKA_OK) return st;
+  const int64_t rows = dims->prefix_len + (append ? dims->chunk_len : 0);
+  if ((st = check_cache(cache, dims, rows, append)) != PKA_OK) return st;
   const size_t need = pka_fwd_workspace_bytes(dims);
   if (need > 0) {
     if (!ws || ws_bytes < need)
@@ -296,9 +297,30 @@ pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k
     p.ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) +
                                         align256((size_t)p.plan.n_split * nrow * dims->head_dim * 4));
   }
+  if (append) {
+    p.append = 1;
+    p.wk = cache->k;
+    p.wv = cache->v;
+    p.wks = static_cast<uint16_t*>(cache->k_scale);
+    p.wvs = static_cast<uint16_t*>(cache->v_scale);
+  }
   hipError_t e = launch_fwd(p, dims->head_dim, cache->type, reinterpret_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "chunk_attn_fwd launch");
+  if (e != hipSuccess) return hip_fail(e, append ? "chunk_attn_fwd_append launch"
+                                                 : "chunk_attn_fwd launch");
   return PKA_OK;
+}
+
+pka_status pka_chunk_attn_fwd(const pka_dims* dims, const void* q, const void* k,
+                              const void* v, const pka_cache* cache, void* o, float* lse,
+                              void* ws, size_t ws_bytes, pka_stream_t stream) {
+  return fwd_common(dims, q, k, v, cache, o, lse, ws, ws_bytes, stream, false);
+}
+
+pka_status pka_chunk_attn_fwd_append(const pka_dims* dims, const void* q, const void* k,
+                                     const void* v, const pka_cache* cache, void* o,
+                                     float* lse, void* ws, size_t ws_bytes,
+                                     pka_stream_t stream) {
+  return fwd_common(dims, q, k, v, cache, o, lse, ws, ws_bytes, stream, true);
 }
 
 pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k,

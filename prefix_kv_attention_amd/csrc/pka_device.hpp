@@ -322,4 +322,95 @@ struct KVStager {
   }
 };
 
+
+// ---------------------------------------------------------------------------
+// Cache writes of the chunk's K/V rows (re-decode into the cache).
+// q8_0 block (32 consecutive values of one token row along head_dim):
+//   amax = max|x|; d = amax / 127 (IEEE fp32 division; the library is built without
+//   fast-math, so '/' is correctly rounded); scale = fp16(d) (RNE);
+//   code = clamp(round_half_away_from_zero(x / d), -127, 127) using the fp32 d;
+//   amax == 0 stores scale 0 and codes 0. Dequantised value = f32(scale) * code.
+__device__ __forceinline__ void q8_0_block(const uint16_t* src, int8_t* dst_codes,
+                                           uint16_t* dst_scale) {
+  float x[32];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const u32x4 w = reinterpret_cast<const u32x4*>(src)[c];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[c * 8 + 2 * e] = bf16_to_f32(w[e] & 0xffffu);
+      x[c * 8 + 2 * e + 1] = bf16_to_f32(w[e] >> 16);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+  const float d = amax / 127.0f;
+  u32x4 q[2];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      int code = 0;
+      if (d != 0.f) {
+        const float r = roundf(x[c * 4 + e] / d);  // halves away from zero
+        code = (int)fminf(fmaxf(r, -127.f), 127.f);
+      }
+      w |= (uint32_t)(code & 0xff) << (8 * e);
+    }
+    q[c >> 2][c & 3] = w;
+  }
+  reinterpret_cast<u32x4*>(dst_codes)[0] = q[0];
+  reinterpret_cast<u32x4*>(dst_codes)[1] = q[1];
+  *dst_scale = f32_to_f16_bits(d);
+}
+
+// 8 bf16 values -> the 16-bit cache type: F16 (round to nearest even) or a copy.
+template <int CT>
+__device__ __forceinline__ u32x4 to_cache16(const u32x4& w) {
+  if constexpr (CT == kF16) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o[e] = (uint32_t)f32_to_f16_bits(bf16_to_f32(w[e] & 0xffffu)) |
+             ((uint32_t)f32_to_f16_bits(bf16_to_f32(w[e] >> 16)) << 16);
+    return o;
+  } else {
+    return w;
+  }
+}
+
+// Number of work items of the append of one (window, KV head): q8_0 blocks of 32
+// values or 16-bit chunks of 8 values, K rows first, then V rows.
+template <int CT, int D>
+__host__ __device__ constexpr int64_t append_items(int64_t C) {
+  return 2 * C * (CT == kQ8 ? D / 32 : D / 8);
+}
+
+// Item `it` of the append of one (window, KV head) whose chunk rows start at kc / vc
+// (bf16 [C][D]) and whose first written cache row is `crow0` (element offset of row
+// P_b of this window and KV head, in rows).
+template <int CT, int D>
+__device__ __forceinline__ void append_item(int64_t it, int64_t C, const uint16_t* kc,
+                                            const uint16_t* vc, void* ck, void* cv,
+                                            uint16_t* cks, uint16_t* cvs, int64_t crow0) {
+  constexpr int PER = CT == kQ8 ? D / 32 : D / 8;
+  const int64_t half = C * PER;
+  const bool is_v = it >= half;
+  const int64_t i = is_v ? it - half : it;
+  const int64_t tok = i / PER;
+  const int part = (int)(i - tok * PER);
+  const int64_t crow = crow0 + tok;
+  if constexpr (CT == kQ8) {
+    const uint16_t* src = (is_v ? vc : kc) + tok * D + part * 32;
+    int8_t* dst = static_cast<int8_t*>(is_v ? cv : ck) + crow * D + part * 32;
+    q8_0_block(src, dst, (is_v ? cvs : cks) + crow * (D / 32) + part);
+  } else {
+    const u32x4 w = *reinterpret_cast<const u32x4*>((is_v ? vc : kc) + tok * D + part * 8);
+    *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(is_v ? cv : ck) + crow * D + part * 8) =
+        to_cache16<CT>(w);
+  }
+}
+
 }  // namespace pka

@@ -46,6 +46,11 @@ struct FwdParams {
   float* lse;
   float* ws_o;    // [n_split][B*Hq*C][D]  (only when n_split > 1)
   float* ws_lse;  // [n_split][B*Hq*C]
+  int append;     // nonzero: also write the chunk's K/V to cache rows [P_b, P_b + C)
+  void* wk;       // the cache as written by the append (same storage as `cache`)
+  void* wv;
+  uint16_t* wks;
+  uint16_t* wvs;
   int B, Hq, Hkv, G;
   int64_t P, C;      // P: the (largest) prefix length
   const int32_t* plens;  // per-window prefix lengths (device) or null

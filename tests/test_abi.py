@@ -29,7 +29,8 @@ def pka():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pka_chunk_attn_fwd", "pka_chunk_attn_bwd", "pka_kv_append_q8_0",
+    for n in ("pka_chunk_attn_fwd", "pka_chunk_attn_fwd_append", "pka_chunk_attn_bwd",
+              "pka_kv_append_q8_0",
               "pka_kv_append_f16", "pka_kv_append_bf16", "pka_kv_dequant_q8_0",
               "pka_fwd_workspace_bytes", "pka_bwd_workspace_bytes", "pka_prefix_kv_grad",
               "pka_prefix_kv_grad_workspace_bytes", "pka_status_string",
@@ -252,3 +253,19 @@ def test_prefix_kv_grad_validation(pka):
     # horizon 0 is valid and writes nothing (no launch, so fake pointers are fine)
     assert call(0)[0] == 0
     assert pka.prefix_kv_grad_workspace_bytes(d, 300) == 0     # invalid -> 0
+
+
+def test_fwd_append_validation(pka):
+    """The fused forward + append needs the capacity of the append (P + C rows)."""
+    lib = pka.lib
+    d = dims(pka, prefix_len=500, chunk_len=64)
+
+    def call(c):
+        st = lib.pka_chunk_attn_fwd_append(ctypes.byref(d), A, A, A, ctypes.byref(c), A, A,
+                                           A, 1 << 40, None)
+        return st, lib.pka_last_error().decode()
+
+    st, msg = call(cache(pka, capacity=563))       # enough for P, not for P + C
+    assert st == 4 and "capacity" in msg
+    assert call(cache(pka, capacity=600, type=pka.CACHE_Q8_0))[0] == 1   # no scales
+    assert call(cache(pka, capacity=600, k=MIS))[0] == 5
