@@ -254,7 +254,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int NK = PREFIX ? (int)p.horizon : C;   // keys of this launch per (b, kv)
   const int nkb = (NK + KB - 1) / KB;
   const int RS = p.plan.n_dkv_split;
-  const int L = blockIdx.x;
+  // Neighbouring logical ids (key blocks of one unit) share an XCD and so read the
+  // unit's Q / dO rows from that XCD's L2.
+  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
   const int rsplit = L % RS;
   const int kblk = (L / RS) % nkb;
   const int grp = L / (RS * nkb);
