@@ -18,12 +18,13 @@
 //                Split over key tiles like the forward when the units are too few;
 //                fp32 partials are summed by bwd_reduce in a fixed order. MFMA
 //                blocks run at raised wave priority (measured ~1.5% faster).
-//  2. bwd_dkdv:  per 64 chunk keys of one (window, KV head), stream the packed
+//  2. bwd_dkdv:  per 128 chunk keys of one (window, KV head), stream the packed
 //                query rows of all G heads that can see them (token >= key) in tiles
 //                of 64: S = Q K^T and dP = dO V^T with keys as MFMA columns, then
 //                dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposing reads).
-//                Waves 0-1 take the first 32 rows of every tile and waves 2-3 the
-//                second 32; the two partial sums are added through LDS at the end.
+//                Each of the 4 waves owns 32 keys and takes both 32-row halves of
+//                every tile (four independent MFMA chains per wave); a staged tile
+//                serves 128 keys, halving the query-row re-reads of 64-key blocks.
 //                The sum over the G heads of a KV head falls out of the packing.
 //                When (window, KV head, key block) units are few, each is split
 //                over disjoint query-row ranges whose fp32 partials
@@ -214,19 +215,14 @@ constexpr int KB = kDkvKeysPerBlock;        // chunk keys per workgroup (64)
 template <int D>
 struct DkvLds {
   static constexpr int S = D + 8;
-  union {
-    struct {
-      uint16_t q[2][BQ * S];
-      uint16_t g[2][BQ * S];   // dO
-    } t;
-    float red[2][32 * D * 2];  // partial dK^T, dV^T of waves 2-3 (fp32)
-  } u;
+  uint16_t q[2][BQ * S];
+  uint16_t g[2][BQ * S];   // dO
   __align__(16) float lse2[2][BQ];
   __align__(16) float dlt[2][BQ];   // -delta of the staged rows
   __align__(16) int tok[2][BQ];
 };
 
-// dK/dV of one block of 64 keys of one (window, KV head), over the packed query
+// dK/dV of one block of 128 keys of one (window, KV head), over the packed query
 // rows of all G heads that see them. PREFIX = false: the chunk's own keys (causal:
 // rows whose token is >= the key), bf16 outputs dk, dv [B][Hkv][C][D].
 // PREFIX = true: the last `horizon` cache rows [P_b - H, P_b) of the window (every
@@ -241,13 +237,12 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
   constexpr int NT = (BQ / 4) * CH;   // staging tasks per tensor (<= 256)
-  static_assert(KB == 64, "two key blocks of 32 per workgroup");
+  static_assert(KB == 32 * 4, "one block of 32 keys per wave");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int kw = wave & 1;       // key block of this wave
-  const int qb = wave >> 1;      // query half of every tile this wave takes
+  const int kw = wave;           // key block of this wave
   const int C = (int)p.C;
   const int G = p.G;
   const int rows = G * C;
@@ -381,8 +376,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     if (stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4*>(&sm.u.t.q[buf][prow(tr0 + i) * S + td0]) = rq[i];
-        *reinterpret_cast<u32x4*>(&sm.u.t.g[buf][prow(tr0 + i) * S + td0]) = rg[i];
+        *reinterpret_cast<u32x4*>(&sm.q[buf][prow(tr0 + i) * S + td0]) = rq[i];
+        *reinterpret_cast<u32x4*>(&sm.g[buf][prow(tr0 + i) * S + td0]) = rg[i];
       }
     }
     if (tid < BQ) {
@@ -392,7 +387,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     }
   };
 
-  const int a_off = prow(l32) * S + hf * 8 + qb * 32 * S;  // this wave's 32 query rows
+  const int a_off = prow(l32) * S + hf * 8;   // + sb * 32 * S: row half sb of a step
   const TrOffsets t_off = tr_lane_offsets<S>(lane);
 
   if (n_steps > 0) {
@@ -405,51 +400,64 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int clean_from = (kblk * KB + KB - 1) * G;
   for (int step = 0; step < n_steps; ++step) {
     const int cur = step & 1;
-    const uint16_t* qt = sm.u.t.q[cur];
-    const uint16_t* gt = sm.u.t.g[cur];
+    const uint16_t* qt = sm.q[cur];
+    const uint16_t* gt = sm.g[cur];
     const bool diag = !PREFIX && r_begin + step * BQ < clean_from;
-    // dP (rows x keys) starts from -delta of its rows, so the chain yields dP - delta;
-    // register i of the result is row (i / 4) * 8 + hf * 4 + i % 4 of the wave's 32.
-    f32x16 s = f32x16{}, dp;
+    // Both 32-row halves of the step against this wave's 32 keys: four independent
+    // MFMA chains. dP (rows x keys) starts from -delta of its rows, so the chain
+    // yields dP - delta; register i of a result is row (i / 4) * 8 + hf * 4 + i % 4 of
+    // its half.
+    f32x16 s[2], dp[2];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qb * 32 + g4 * 8 + hf * 4]);
+    for (int sb = 0; sb < 2; ++sb) {
+      s[sb] = f32x16{};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dp[g4 * 4 + j] = d4[j];
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][sb * 32 + g4 * 8 + hf * 4]);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      s = mfma32(*reinterpret_cast<const bf16x8*>(&qt[a_off + ks * 16]), kreg[ks], s);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(&gt[a_off + ks * 16]), vreg[ks], dp);
-    }
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // result rows (g4*8 + hf*4 + 0..3) of this wave's 32 query rows: one 16-byte
-      // read per per-row array
-      const int q0 = qb * 32 + g4 * 8 + hf * 4;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
-      const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
-      const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = g4 * 4 + j;
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[i], c, -l4[j]));
-        // Prefix keys are seen by every row; padding rows past the last one have
-        // zero q and dO and so add nothing. Chunk keys: causal, checked only in the
-        // steps that reach below the block's last key.
-        const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
-        pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
+        for (int j = 0; j < 4; ++j) dp[sb][g4 * 4 + j] = d4[j];
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int o = a_off + sb * 32 * S + ks * 16;
+        s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(&qt[o]), kreg[ks], s[sb]);
+        dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(&gt[o]), vreg[ks], dp[sb]);
+      }
+    bf16x8 pb[2][2], dsb[2][2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // result rows (g4*8 + hf*4 + 0..3) of row half sb: one 16-byte read per
+        // per-row array
+        const int q0 = sb * 32 + g4 * 8 + hf * 4;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+        const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
+        const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = g4 * 4 + j;
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -l4[j]));
+          // Prefix keys are seen by every row; padding rows past the last one have
+          // zero q and dO and so add nothing. Chunk keys: causal, checked only in
+          // the steps that reach below the block's last key.
+          const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
+          pb[sb][i >> 3][i & 7] = (__bf16)pv;
+          dsb[sb][i >> 3][i & 7] = (__bf16)(pv * dp[sb][i]);
+        }
+      }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, qb * 32 + ss * 16, db * 32), pb[ss], accv[db]);
-        acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, qb * 32 + ss * 16, db * 32), dsb[ss], acck[db]);
-      }
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+          accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, sb * 32 + ss * 16, db * 32), pb[sb][ss], accv[db]);
+          acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, sb * 32 + ss * 16, db * 32), dsb[sb][ss], acck[db]);
+        }
     if (step + 1 < n_steps) {
       stage(cur ^ 1);
       if (step + 2 < n_steps) issue(step + 2);
@@ -457,27 +465,15 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  // Waves 2-3 hand their partial sums to waves 0-1 through LDS (fp32, fixed order).
-  float* red = sm.u.red[kw];
-  if (qb == 1) {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[(db * 16 + i) * 64 + lane] = acck[db][i];
-        red[32 * D + (db * 16 + i) * 64 + lane] = accv[db][i];
-      }
-  }
-  __syncthreads();
-  if (qb == 1 || key >= NK) return;
+  if (key >= NK) return;
   // A prefix row that does not exist (P_b < H) gets an exact zero.
+  if (!key_ok) {
 #pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acck[db][i] = key_ok ? acck[db][i] + red[(db * 16 + i) * 64 + lane] : 0.f;
-      accv[db][i] = key_ok ? accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane] : 0.f;
+    for (int db = 0; db < NDB; ++db) {
+      acck[db] = f32x16{};
+      accv[db] = f32x16{};
     }
+  }
   const float sc = p.scale;
   if (PREFIX && RS == 1) {
     float* pk = p.dkp + (bh * NK + key) * D;

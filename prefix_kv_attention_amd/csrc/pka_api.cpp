@@ -193,7 +193,7 @@ Plan plan_bwd(const pka_dims& d) {
   return pl;
 }
 
-// Prefix gradient: one unit per (window, KV head, block of 64 prefix keys of the
+// Prefix gradient: one unit per (window, KV head, block of 128 prefix keys of the
 // horizon), split over query rows like the chunk dK/dV when units are few.
 Plan plan_prefix_kv(const pka_dims& d, int64_t horizon) {
   Plan pl{};

@@ -16,7 +16,7 @@ constexpr int kWavesPerBlock = PKA_WAVES_PER_BLOCK;   // waves per forward / dQ 
 constexpr int kBlocksPerCU = 8 / kWavesPerBlock;      // resident forward / dQ workgroups per CU
 constexpr int kRowsPerBlock = 32 * kWavesPerBlock;  // packed query rows per workgroup
 constexpr int kKeysPerTile = 64;    // keys staged in LDS per step
-constexpr int kDkvKeysPerBlock = 64;   // chunk keys per dK/dV workgroup (2 x 32)
+constexpr int kDkvKeysPerBlock = 128;  // keys per dK/dV workgroup (4 waves x 32)
 constexpr int kNumCUs = 256;        // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXCDs = 8;
 
