@@ -201,11 +201,16 @@ const char* pka_status_string(pka_status status);
 /* The message of the last failed call on this thread ("" if none). */
 const char* pka_last_error(void);
 
-/* Opt-in kernel timing for benchmarks. When enabled, each kernel launch is
- * bracketed by two HIP events recorded on the call's stream; pka_profile_read
- * synchronises on those events and returns the summed elapsed milliseconds and
- * the number of launches of one kernel since the last reset. At most 65536 launches
- * per kernel are recorded between resets (later ones are counted in `dropped`). */
+/* Opt-in kernel timing for benchmarks. When enabled, each launch of a selected
+ * kernel is bracketed by two HIP events recorded on the call's stream;
+ * pka_profile_read synchronises on those events and returns the summed elapsed
+ * milliseconds and the number of launches of one kernel since the last reset. At
+ * most 65536 launches per kernel are recorded between resets (later ones are
+ * counted in `dropped`). pka_profile_select limits the bracketing to the kernels
+ * whose bit (1u << pka_kernel_id) is set in kernel_mask (after load: all), so a
+ * timed loop can carry the events of one kernel only. Enable and select are
+ * process-wide settings; changing them while another thread launches affects
+ * that thread's next launches only. */
 typedef enum {
   PKA_KERNEL_FWD = 0,        /* forward tiles (one launch per pka_chunk_attn_fwd) */
   PKA_KERNEL_FWD_COMBINE = 1,/* merge of prefix splits                            */
@@ -222,6 +227,7 @@ typedef enum {
 } pka_kernel_id;
 
 pka_status pka_profile_enable(int32_t on);
+pka_status pka_profile_select(uint32_t kernel_mask);
 pka_status pka_profile_reset(void);
 pka_status pka_profile_read(int32_t kernel, double* total_ms, int64_t* launches,
                             int64_t* dropped);

@@ -76,6 +76,7 @@ _SIGS = {
     "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pka_last_error": (ctypes.c_char_p, []),
     "pka_profile_enable": (ctypes.c_int, [_i32]),
+    "pka_profile_select": (ctypes.c_int, [ctypes.c_uint32]),
     "pka_profile_reset": (ctypes.c_int, []),
     "pka_profile_read": (ctypes.c_int, [_i32, _P(ctypes.c_double), _P(_i64), _P(_i64)]),
 }
@@ -396,6 +397,12 @@ class WindowWalk:
 
 def profile_enable(on: bool = True):
     _check(_lib.pka_profile_enable(1 if on else 0), "pka_profile_enable")
+
+
+def profile_select(kernels=None):
+    """Bracket only the named kernels (None: all) while profiling is enabled."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNELS[k] for k in kernels)
+    _check(_lib.pka_profile_select(mask), "pka_profile_select")
 
 
 def profile_reset():

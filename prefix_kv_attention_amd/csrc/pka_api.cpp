@@ -3,6 +3,7 @@
 // contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -110,15 +111,19 @@ struct ProfSlot {
   std::vector<hipEvent_t> begin, end;  // pooled events, reused across resets
   int64_t used = 0;
   int64_t dropped = 0;
+  bool open = false;                   // a begin event was recorded, its end not yet
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+std::atomic<bool> g_prof_on{false};
+std::atomic<uint32_t> g_prof_mask{0xFFFFFFFFu};   // kernels bracketed while enabled
 ProfSlot g_prof[PKA_KERNEL_COUNT];
 
 }  // namespace
 
 void prof_begin(int kernel, hipStream_t s) {
-  if (!g_prof_on) return;
+  if (!g_prof_on.load(std::memory_order_relaxed) ||
+      !((g_prof_mask.load(std::memory_order_relaxed) >> kernel) & 1u))
+    return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfSlot& sl = g_prof[kernel];
   if (sl.used >= kMaxRecords) {
@@ -135,16 +140,15 @@ void prof_begin(int kernel, hipStream_t s) {
     sl.begin.push_back(a);
     sl.end.push_back(b);
   }
-  (void)hipEventRecord(sl.begin[sl.used], s);
+  sl.open = hipEventRecord(sl.begin[sl.used], s) == hipSuccess;
 }
 
 void prof_end(int kernel, hipStream_t s) {
-  if (!g_prof_on) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   ProfSlot& sl = g_prof[kernel];
-  if (sl.used >= kMaxRecords || (int64_t)sl.end.size() <= sl.used) return;
-  (void)hipEventRecord(sl.end[sl.used], s);
-  ++sl.used;
+  if (!sl.open) return;   // its begin was not recorded (off, not selected, or full)
+  sl.open = false;
+  if (hipEventRecord(sl.end[sl.used], s) == hipSuccess) ++sl.used;
 }
 
 // One row block is kRowsPerBlock packed rows of one (window, KV head) and runs as
@@ -526,8 +530,12 @@ pka_status pka_kv_dequant_q8_0(const pka_cache* cache, int32_t batch, int32_t n_
 }
 
 pka_status pka_profile_enable(int32_t on) {
-  std::lock_guard<std::mutex> lk(g_prof_mu);
-  g_prof_on = on != 0;
+  g_prof_on.store(on != 0);
+  return PKA_OK;
+}
+
+pka_status pka_profile_select(uint32_t kernel_mask) {
+  g_prof_mask.store(kernel_mask);
   return PKA_OK;
 }
 
@@ -536,6 +544,7 @@ pka_status pka_profile_reset(void) {
   for (auto& sl : g_prof) {
     sl.used = 0;
     sl.dropped = 0;
+    sl.open = false;
   }
   return PKA_OK;
 }
