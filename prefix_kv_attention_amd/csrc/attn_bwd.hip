@@ -210,7 +210,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
 
 // ------------------------------------------------------------------ dK / dV
 constexpr int BQ = 64;                      // packed query rows per step
-constexpr int KB = kDkvKeysPerBlock;        // chunk keys per workgroup (64)
+constexpr int KB = kDkvKeysPerBlock;        // keys per dK/dV workgroup (128)
 
 template <int D>
 struct DkvLds {
@@ -248,13 +248,25 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int rows = G * C;
   const int NK = PREFIX ? (int)p.horizon : C;   // keys of this launch per (b, kv)
   const int nkb = (NK + KB - 1) / KB;
-  const int RS = p.plan.n_dkv_split;
+  const int RS = p.plan.n_dkv_split;   // > 1: partials for bwd_reduce
   // Neighbouring logical ids (key blocks of one unit) share an XCD and so read the
   // unit's Q / dO rows from that XCD's L2.
   const int L = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int rsplit = L % RS;
-  const int kblk = (L / RS) % nkb;
-  const int grp = L / (RS * nkb);
+  int rsplit, kblk, grp, RSk;   // RSk: row splits of this key block
+  if (!PREFIX && p.plan.dkv_nkb > 0) {
+    const int per = p.plan.dkv_first[nkb];
+    grp = L / per;
+    const int r = L - grp * per;
+    kblk = 0;
+    while (kblk + 1 < nkb && p.plan.dkv_first[kblk + 1] <= r) ++kblk;
+    rsplit = r - p.plan.dkv_first[kblk];
+    RSk = p.plan.dkv_first[kblk + 1] - p.plan.dkv_first[kblk];
+  } else {
+    rsplit = L % RS;
+    kblk = (L / RS) % nkb;
+    grp = L / (RS * nkb);
+    RSk = RS;
+  }
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
 
@@ -307,8 +319,8 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   // Rows whose token is >= the block's first key can see some key of it.
   const int r_unit = PREFIX ? 0 : kblk * KB * G;
   const int steps_unit = (rows - r_unit + BQ - 1) / BQ;
-  const int s_lo = (int)((int64_t)rsplit * steps_unit / RS);
-  const int s_hi = (int)((int64_t)(rsplit + 1) * steps_unit / RS);
+  const int s_lo = (int)((int64_t)rsplit * steps_unit / RSk);
+  const int s_hi = (int)((int64_t)(rsplit + 1) * steps_unit / RSk);
   const int r_begin = r_unit + s_lo * BQ;   // this split's rows
   const int n_steps = s_hi - s_lo;
   const bool stager = tid < NT;
@@ -560,6 +572,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdParams p, int64_t n_
     src = p.ws_dkv + (which * nkey + row) * D + c8 * 8;
     stride = 2 * nkey * D;
     nsplit = p.plan.n_dkv_split;
+    if (!F32OUT && p.plan.dkv_nkb > 0) {   // chunk keys: splits of the row's key block
+      const int kb = (int)((row % nk) / KB);
+      nsplit = p.plan.dkv_first[kb + 1] - p.plan.dkv_first[kb];
+    }
     if (F32OUT)
       dst32 = (which ? p.dvp : p.dkp) + row * D + c8 * 8;
     else
@@ -594,9 +610,10 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   const int nkb = (int)((p.C + KB - 1) / KB);
+  const int per_grp = p.plan.dkv_nkb > 0 ? p.plan.dkv_first[nkb] : nkb * p.plan.n_dkv_split;
   prof_begin(PKA_KERNEL_BWD_DKDV, s);
-  hipLaunchKernelGGL((bwd_kv_kernel<D, kBF16, false>),
-                     dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<D, kBF16, false>), dim3(p.B * p.Hkv * per_grp),
+                     dim3(256), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DKDV, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 

@@ -157,7 +157,7 @@ void prof_end(int kernel, hipStream_t s) {
 // workgroups; each split keeps at least 8 tiles so the merge stays small next to
 // the work.
 static Plan make_plan(const pka_dims& d) {
-  Plan pl;
+  Plan pl{};
   const int64_t G = d.n_heads_q / d.n_heads_kv;
   pl.n_rb = (int)((G * d.chunk_len + kRowsPerBlock - 1) / kRowsPerBlock);
   const int64_t units = (int64_t)d.batch * d.n_heads_kv * pl.n_rb;
@@ -177,22 +177,58 @@ static Plan make_plan(const pka_dims& d) {
 
 Plan plan_fwd(const pka_dims& d) { return make_plan(d); }
 
-// dK/dV: one unit per (window, KV head, block of kDkvKeysPerBlock chunk keys). Few
-// units are split over disjoint ranges of query rows (each split keeps >= 2 steps
-// of 64 rows of the longest unit); their fp32 partials are summed afterwards.
+// dK/dV: one unit per (window, KV head, block of kDkvKeysPerBlock chunk keys). When
+// units are fewer than the CUs, they are split over disjoint ranges of query rows
+// (each split keeps >= 2 steps of 64 rows, at most 16 splits) and the fp32 partials
+// are summed afterwards. Key block k is seen only by the rows of tokens >= its first
+// key, so the splits go where the rows are: starting from one per block, each
+// further split of the CU budget goes to the block whose workgroups have the most
+// steps (the first such block on ties).
 Plan plan_bwd(const pka_dims& d) {
   Plan pl = make_plan(d);
   const int64_t G = d.n_heads_q / d.n_heads_kv;
   const int64_t nkb = (d.chunk_len + kDkvKeysPerBlock - 1) / kDkvKeysPerBlock;
-  const int64_t units = (int64_t)d.batch * d.n_heads_kv * nkb;
-  int64_t split = 1;
-  if (units < kNumCUs) {
-    split = kNumCUs / units;
-    const int64_t max_steps = (G * d.chunk_len + 63) / 64;
-    const int64_t max_split = max_steps / 2 > 1 ? max_steps / 2 : 1;
-    if (split > max_split) split = max_split;
-    if (split > 16) split = 16;
+  const int64_t groups = (int64_t)d.batch * d.n_heads_kv;
+  const int64_t units = groups * nkb;
+  pl.n_dkv_split = 1;
+  pl.dkv_nkb = 0;
+  if (units >= kNumCUs) return pl;
+  if (nkb <= kMaxDkvTable) {
+    int64_t steps[kMaxDkvTable], cnt[kMaxDkvTable];
+    for (int64_t k = 0; k < nkb; ++k) {
+      steps[k] = (G * (d.chunk_len - k * kDkvKeysPerBlock) + 63) / 64;
+      cnt[k] = 1;
+    }
+    for (int64_t left = kNumCUs / groups - nkb; left > 0; --left) {
+      int64_t best = -1, best_load = 0;
+      for (int64_t k = 0; k < nkb; ++k) {
+        const int64_t cap = steps[k] / 2 < 16 ? steps[k] / 2 : 16;
+        if (cnt[k] >= cap) continue;
+        const int64_t load = (steps[k] + cnt[k] - 1) / cnt[k];
+        if (load > best_load) {
+          best = k;
+          best_load = load;
+        }
+      }
+      if (best < 0) break;
+      ++cnt[best];
+    }
+    int64_t first = 0, most = 1;
+    for (int64_t k = 0; k < nkb; ++k) {
+      pl.dkv_first[k] = (int16_t)first;
+      first += cnt[k];
+      if (cnt[k] > most) most = cnt[k];
+    }
+    pl.dkv_first[nkb] = (int16_t)first;
+    pl.dkv_nkb = (int)nkb;
+    pl.n_dkv_split = (int)most;
+    return pl;
   }
+  int64_t split = kNumCUs / units;
+  const int64_t max_steps = (G * d.chunk_len + 63) / 64;
+  const int64_t max_split = max_steps / 2 > 1 ? max_steps / 2 : 1;
+  if (split > max_split) split = max_split;
+  if (split > 16) split = 16;
   pl.n_dkv_split = (int)split;
   return pl;
 }

@@ -9,11 +9,8 @@
 namespace pka {
 
 // Tile geometry shared by host planning and kernels.
-#ifndef PKA_WAVES_PER_BLOCK
-#define PKA_WAVES_PER_BLOCK 8
-#endif
-constexpr int kWavesPerBlock = PKA_WAVES_PER_BLOCK;   // waves per forward / dQ workgroup
-constexpr int kBlocksPerCU = 8 / kWavesPerBlock;      // resident forward / dQ workgroups per CU
+constexpr int kWavesPerBlock = 8;   // waves per forward / dQ workgroup (2 per SIMD)
+constexpr int kBlocksPerCU = 1;     // resident forward / dQ workgroups per CU
 constexpr int kRowsPerBlock = 32 * kWavesPerBlock;  // packed query rows per workgroup
 constexpr int kKeysPerTile = 64;    // keys staged in LDS per step
 constexpr int kDkvKeysPerBlock = 128;  // keys per dK/dV workgroup (4 waves x 32)
@@ -30,11 +27,20 @@ struct CacheRef {
 };
 
 // Work plan of the forward / dQ grids: units of (window, KV head, row block, split).
+constexpr int kMaxDkvTable = 64;   // chunk key blocks with their own split counts
+
 struct Plan {
   int n_rb;     // row blocks of kRowsPerBlock packed rows per (window, KV head)
   int n_split;  // prefix splits per row block
   int nblk;     // workgroups = B * Hkv * n_rb * n_split
-  int n_dkv_split;  // backward only: query-row splits per dK/dV key block
+  int n_dkv_split;  // backward only: query-row splits per dK/dV key block (the most
+                    // of any block; > 1 means every block writes fp32 partials)
+  // Chunk dK/dV with causal work per key block: block k is seen by G*(C - k*128)
+  // packed rows, so it gets its own number of row splits. dkv_nkb > 0: block k
+  // has splits [dkv_first[k], dkv_first[k + 1]) of the dkv_first[dkv_nkb] workgroups
+  // of each (window, KV head). dkv_nkb == 0: every block has n_dkv_split splits.
+  int dkv_nkb;
+  int16_t dkv_first[kMaxDkvTable + 1];
 };
 
 struct FwdParams {
