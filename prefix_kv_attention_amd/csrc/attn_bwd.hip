@@ -144,11 +144,20 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
       // dP^T starts from -delta (this lane's row), so the chain yields dP - delta.
       f32x16 st = f32x16{}, dpt = ndlt;
       __builtin_amdgcn_s_setprio(1);
+      {
+        bf16x8 a[NKS][2];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int off = k_off + kb * 32 * S + ks * 16;
-        st = mfma32(*reinterpret_cast<const bf16x8*>(&kt[off]), qreg[ks], st);
-        dpt = mfma32(*reinterpret_cast<const bf16x8*>(&vt[off]), oreg[ks], dpt);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const int off = k_off + kb * 32 * S + ks * 16;
+          a[ks][0] = *reinterpret_cast<const bf16x8*>(&kt[off]);
+          a[ks][1] = *reinterpret_cast<const bf16x8*>(&vt[off]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          st = mfma32(a[ks][0], qreg[ks], st);
+          dpt = mfma32(a[ks][1], oreg[ks], dpt);
+        }
+        sched_ahead<2 * NKS, kDqReadAheadSP, 1>();
       }
       __builtin_amdgcn_s_setprio(0);
       if (masked) {
@@ -164,11 +173,18 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
         dsb[i >> 3][i & 7] = (__bf16)(pv * dpt[i]);
       }
       __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      {
+        bf16x8 a[2][NDB];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          acc[db] = mfma32(lds_tr_operand<S>(kt, t_off, kb * 32 + s * 16, db * 32), dsb[s], acc[db]);
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) a[s][db] = lds_tr_operand<S>(kt, t_off, kb * 32 + s * 16, db * 32);
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) acc[db] = mfma32(a[s][db], dsb[s], acc[db]);
+        sched_ahead<2 * NDB, kDqReadAheadDQ, 2>();
+      }
       __builtin_amdgcn_s_setprio(0);
     }
 

@@ -114,15 +114,19 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   // work fills in behind it (measured: a few percent faster than equal priority).
   auto scores = [&](const uint16_t* kt, f32x16 (&st)[2]) {
     __builtin_amdgcn_s_setprio(1);
+    bf16x8 a[NKS][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      st[kb] = f32x16{};
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
-        st[kb] = mfma32(a, qreg[ks], st[kb]);
-      }
-    }
+      for (int kb = 0; kb < 2; ++kb)
+        a[ks][kb] = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) st[kb] = mfma32(a[ks][kb], qreg[ks], st[kb]);
+    sched_ahead<2 * NKS, kFwdReadAhead, 1>();
     __builtin_amdgcn_s_setprio(0);
   };
   // Online softmax of one tile. The probabilities are taken against the running
@@ -179,11 +183,16 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   };
   auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4]) {
     __builtin_amdgcn_s_setprio(1);
+    bf16x8 a[NDB][4];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc[db] = mfma32(lds_tr_operand<S>(vt, v_off, kk * 16, db * 32), pb[kk], acc[db]);
+      for (int db = 0; db < NDB; ++db) a[db][kk] = lds_tr_operand<S>(vt, v_off, kk * 16, db * 32);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc[db] = mfma32(a[db][kk], pb[kk], acc[db]);
+    sched_ahead<4 * NDB, kFwdReadAhead, 2>();
     __builtin_amdgcn_s_setprio(0);
   };
 

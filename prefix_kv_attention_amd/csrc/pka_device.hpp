@@ -140,6 +140,31 @@ __device__ __forceinline__ int xcd_logical_id(int i, int nblk) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
+// Instruction order of an unrolled chain of N MFMAs whose A operands take R LDS
+// reads each: the reads run PF MFMAs ahead of their use (scheduling-group barriers;
+// masks 0x100 = LDS reads, 0x008 = MFMA). Without it the compiler issues each
+// operand read right before its MFMA, and the wave waits out the LDS latency.
+template <int I, int N, int R>
+__device__ __forceinline__ void sched_rep_mr() {
+  if constexpr (I < N) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+    sched_rep_mr<I + 1, N, R>();
+  }
+}
+template <int N, int PF, int R>
+__device__ __forceinline__ void sched_ahead() {
+  __builtin_amdgcn_sched_group_barrier(0x100, R * PF, 0);
+  sched_rep_mr<0, N - PF, R>();
+  __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+}
+
+// Read-ahead depths (MFMAs), measured: the forward's S and P V chains 6; the dQ
+// kernel's S / dP chains 4 and its dQ chain 3 (it has no registers for more).
+constexpr int kFwdReadAhead = 6;
+constexpr int kDqReadAheadSP = 4;
+constexpr int kDqReadAheadDQ = 3;
+
 // Wait until every global load this wave issued has returned (s_waitcnt vmcnt(0)).
 // Used once after a kernel's prologue: the compiler cannot tell at the loop header
 // whether the one-time operand loads (Q, dO) are still in flight, and otherwise
