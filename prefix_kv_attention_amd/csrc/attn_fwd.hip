@@ -181,18 +181,20 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
     }
     l += lt;
   };
-  auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4]) {
+  // P V operands: the first kPre are read before the softmax (they do not depend on
+  // it), the rest kFwdReadAhead MFMAs ahead of their use.
+  constexpr int NPV = 4 * NDB;
+  constexpr int kPre = kFwdPvEarlyReads;
+  auto pv_operand = [&](const uint16_t* vt, int i) __attribute__((always_inline)) {
+    return lds_tr_operand<S>(vt, v_off, (i / NDB) * 16, (i % NDB) * 32);
+  };
+  auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4], bf16x8 (&a)[NPV]) {
     __builtin_amdgcn_s_setprio(1);
-    bf16x8 a[NDB][4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int i = kPre; i < NPV; ++i) a[i] = pv_operand(vt, i);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) a[db][kk] = lds_tr_operand<S>(vt, v_off, kk * 16, db * 32);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) acc[db] = mfma32(a[db][kk], pb[kk], acc[db]);
-    sched_ahead<4 * NDB, kFwdReadAhead, 2>();
+    for (int i = 0; i < NPV; ++i) acc[i % NDB] = mfma32(a[i], pb[i / NDB], acc[i % NDB]);
+    sched_ahead_after<NPV, kPre, kFwdReadAhead, 2>();
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -207,9 +209,12 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
     const int cur = (tile - tb) & 1;
     f32x16 st[2];
     scores(sm.k[cur], st);
+    bf16x8 pva[NPV];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) pva[i] = pv_operand(sm.v[cur], i);
     bf16x8 pb[4];
     softmax(st, tile, pb);
-    pv_mfma(sm.v[cur], pb);
+    pv_mfma(sm.v[cur], pb, pva);
     if (tile + 1 < te) {
       stg.store(sm.k[cur ^ 1], sm.v[cur ^ 1]);
       if (tile + 2 < te) stg.issue(tile + 2);

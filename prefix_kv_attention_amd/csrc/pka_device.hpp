@@ -159,9 +159,20 @@ __device__ __forceinline__ void sched_ahead() {
   __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
 }
 
-// Read-ahead depths (MFMAs), measured: the forward's S and P V chains 6; the dQ
-// kernel's S / dP chains 4 and its dQ chain 3 (it has no registers for more).
+// As sched_ahead, for a chain whose first PRE operands were read earlier (before
+// other work): the remaining reads run PF MFMAs ahead.
+template <int N, int PRE, int PF, int R>
+__device__ __forceinline__ void sched_ahead_after() {
+  constexpr int LEAD = PF > PRE ? PF - PRE : 0;   // reads to issue before the first MFMA
+  if constexpr (LEAD > 0) __builtin_amdgcn_sched_group_barrier(0x100, R * LEAD, 0);
+  sched_rep_mr<0, N - PRE - LEAD, R>();
+  __builtin_amdgcn_sched_group_barrier(0x008, PRE + LEAD, 0);
+}
+// Read-ahead depths (MFMAs), measured: the forward's S and P V chains 6 (the first
+// 4 P V operands read before the softmax); the dQ kernel's S / dP chains 4 and its
+// dQ chain 3 (it has no registers for more).
 constexpr int kFwdReadAhead = 6;
+constexpr int kFwdPvEarlyReads = 4;
 constexpr int kDqReadAheadSP = 4;
 constexpr int kDqReadAheadDQ = 3;
 
