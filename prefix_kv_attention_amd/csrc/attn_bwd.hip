@@ -368,40 +368,47 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     }
   };
   u32x4 rq[4], rg[4];
-  float pl = 0.f, pd = 0.f;
-  int ptok = -1;
+  float pl = 0.f, pd = 0.f;   // raw LSE and delta of the staged row: they are scaled
+  int ptok = -1;              // when written to LDS, a step after their loads
+  int rows_left = 0;          // rows of the issued step that exist (>= BQ: all)
   auto issue = [&](int step) {   // called for steps 0, 1, 2, ... in order
     const int r0 = r_begin + step * BQ;
+    // LSE / delta first: the loads complete in order, so a wait that the compiler
+    // may place for them does not also wait for the row loads below.
+    if (tid < BQ) {
+      // Unconditional loads (a padding row reads token 0 of the first head): any
+      // use of a loaded value here would wait for every load in flight.
+      const bool valid = r0 + tid < rows;
+      const int64_t row = valid ? (head0 + gl) * C + tl : head0 * C;
+      pl = p.lse[row];
+      pd = p.delta[row];
+      ptok = valid ? tl : -1;
+      advance(tl, gl);
+    }
+    // Rows past the last one (only in the last step) load a valid row and are zeroed
+    // when staged: no register is written here but by the loads themselves.
+    rows_left = rows - r0;
     if (stager) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (r0 + tr0 + i < rows) {
-          const int64_t row = (head0 + gq[i]) * C + tq[i];
-          rq[i] = *reinterpret_cast<const u32x4*>(p.q + row * D + td0);
-          rg[i] = *reinterpret_cast<const u32x4*>(p.d_o + row * D + td0);
-        } else {
-          rq[i] = u32x4{0u, 0u, 0u, 0u};
-          rg[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const bool ok = tr0 + i < rows_left;
+        const int64_t row = ok ? (head0 + gq[i]) * C + tq[i] : head0 * C;
+        rq[i] = *reinterpret_cast<const u32x4*>(p.q + row * D + td0);
+        rg[i] = *reinterpret_cast<const u32x4*>(p.d_o + row * D + td0);
         advance(tq[i], gq[i]);
       }
-    }
-    if (tid < BQ) {
-      if (r0 + tid < rows) {
-        const int64_t row = (head0 + gl) * C + tl;
-        pl = p.lse[row] * kLog2e;
-        pd = -p.delta[row];   // staged negated: the dP^T chain starts from it
-        ptok = tl;
-      } else {
-        pl = 0.f;
-        pd = 0.f;
-        ptok = -1;
-      }
-      advance(tl, gl);
     }
   };
   auto stage = [&](int buf) {
     if (stager) {
+      if (rows_left < BQ) {   // the last step: zero the rows past the end
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tr0 + i >= rows_left) {
+            rq[i] = u32x4{0u, 0u, 0u, 0u};
+            rg[i] = u32x4{0u, 0u, 0u, 0u};
+          }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         *reinterpret_cast<u32x4*>(&sm.q[buf][prow(tr0 + i) * S + td0]) = rq[i];
@@ -409,8 +416,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
       }
     }
     if (tid < BQ) {
-      sm.lse2[buf][tid] = pl;
-      sm.dlt[buf][tid] = pd;
+      const bool valid = ptok >= 0;
+      sm.lse2[buf][tid] = valid ? pl * kLog2e : 0.f;
+      sm.dlt[buf][tid] = valid ? -pd : 0.f;   // negated: the dP^T chain starts from it
       sm.tok[buf][tid] = ptok;
     }
   };
@@ -424,6 +432,10 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     if (n_steps > 1) issue(1);
     __syncthreads();
   }
+  // One wait for every load so far (K / V rows, step 1's rows): otherwise the
+  // compiler waits at the loop top on each iteration, and that wait also covers the
+  // rows just requested for two steps ahead.
+  wait_global_loads();
   // Packed rows from clean_from on have tokens >= the block's last key: no mask.
   const int clean_from = (kblk * KB + KB - 1) * G;
   for (int step = 0; step < n_steps; ++step) {
