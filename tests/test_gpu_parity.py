@@ -47,8 +47,8 @@ EDGE = [
     synthetic.small("g6-c512", batch=1, prefix_len=1500, chunk_len=512, n_heads_q=6,
                     n_heads_kv=1, head_dim=128, cache_type="q8_0", qkv_std=0.1,
                     prefix_std=1.0, do_std=1e-2, outlier_frac=0.01),
-    # prefix split of dQ without a row split of dK/dV (64 dQ units, 256 dK/dV units)
-    synthetic.small("dq-split-only", batch=2, prefix_len=2048, chunk_len=1024, n_heads_q=8,
+    # prefix split of dQ without a row split of dK/dV (128 dQ units, 256 dK/dV units)
+    synthetic.small("dq-split-only", batch=2, prefix_len=2048, chunk_len=2048, n_heads_q=8,
                     n_heads_kv=8, head_dim=64, cache_type="bf16", qkv_std=0.3, prefix_std=0.3),
     # row split of dK/dV without a prefix split of dQ (256 dQ units, 64 dK/dV units)
     synthetic.small("dkv-split-only", batch=8, prefix_len=128, chunk_len=64, n_heads_q=128,
