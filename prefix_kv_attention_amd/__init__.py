@@ -6,9 +6,10 @@ provides device memory and the current HIP stream. Importing this package raises
 if the library is missing; there is no fallback implementation.
 
 Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
-``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``, ``kv_append_f16``,
-``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``, ``fwd_workspace_bytes``,
-``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``. ``chunk_attention`` wraps forward and backward in an
+``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``,
+``kv_append_f16``, ``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``,
+``fwd_workspace_bytes``, ``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``,
+``profile_*``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
 constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
 chunk loop of a batch of windows: step, append, advance every window's prefix.
@@ -16,6 +17,10 @@ chunk loop of a batch of windows: step, append, advance every window's prefix.
 Every call takes ``prefix_len`` (an int: the prefix of every window, or the
 largest one) and optionally ``prefix_lens``, a CUDA int32 tensor [B] of the
 windows' own prefix lengths (ragged windows; entries clamped to [0, prefix_len]).
+
+The C entry points take bare device pointers and cannot see tensor sizes, so every
+tensor is checked here (shape, dtype, device, contiguity) before the call: a wrong
+one raises ValueError and nothing is launched.
 """
 from __future__ import annotations
 
@@ -125,9 +130,29 @@ class PrefixCache:
     def __init__(self, cache_type: str, k, v, k_scale=None, v_scale=None):
         if cache_type not in CACHE_TYPE_BY_NAME:
             raise ValueError(f"unknown cache type {cache_type!r}")
+        if not isinstance(k, torch.Tensor) or k.dim() != 4:
+            raise ValueError("cache k must be a 4-D tensor [B][Hkv][capacity][D]")
+        dt = {"q8_0": torch.int8, "f16": torch.float16, "bf16": torch.bfloat16}[cache_type]
+        _tensor(k, "cache k", k.shape, dt, k.device)
+        _tensor(v, "cache v", k.shape, dt, k.device)
+        if cache_type == "q8_0":
+            sshape = tuple(k.shape[:3]) + (k.shape[3] // 32,)
+            _tensor(k_scale, "cache k_scale", sshape, torch.float16, k.device)
+            _tensor(v_scale, "cache v_scale", sshape, torch.float16, k.device)
+        elif k_scale is not None or v_scale is not None:
+            raise ValueError(f"a {cache_type} cache has no scales")
         self.cache_type = cache_type
         self.k, self.v, self.k_scale, self.v_scale = k, v, k_scale, v_scale
         self.batch, self.n_heads_kv, self.capacity, self.head_dim = k.shape
+
+    def check_for(self, batch, n_heads_kv, head_dim, device):
+        """Raise unless this cache serves windows of these dimensions on `device`."""
+        if (self.batch, self.n_heads_kv, self.head_dim) != (batch, n_heads_kv, head_dim):
+            raise ValueError(f"cache is [B={self.batch}][Hkv={self.n_heads_kv}][.]"
+                             f"[D={self.head_dim}], the call needs [B={batch}]"
+                             f"[Hkv={n_heads_kv}][.][D={head_dim}]")
+        if self.k.device != device:
+            raise ValueError(f"cache is on {self.k.device}, the call on {device}")
 
     @classmethod
     def empty(cls, cache_type, batch, n_heads_kv, capacity, head_dim, device="cuda"):
@@ -150,15 +175,43 @@ class PrefixCache:
                          self.v_scale.data_ptr() if self.v_scale is not None else None)
 
 
-def _chunk_dims(q, k, prefix_len, scale, prefix_lens=None):
+def _tensor(t, name, shape, dtype, device):
+    """Raise unless t is a contiguous `dtype` CUDA tensor of `shape` on `device`."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _ws_bytes(ws, device):
+    """Size in bytes of a caller's workspace tensor (None: 0)."""
+    if ws is None:
+        return 0
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or ws.device != device \
+            or not ws.is_contiguous():
+        raise ValueError(f"ws must be a contiguous tensor on {device}")
+    return ws.numel() * ws.element_size()
+
+
+def _chunk_inputs(q, k, v, cache, prefix_len, scale, prefix_lens):
+    """Check q [B][Hq][C][D], k and v [B][Hkv][C][D] (bf16) against each other and the
+    cache; return the dims of the call."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or not isinstance(k, torch.Tensor) \
+            or k.dim() != 4:
+        raise ValueError("q and k must be 4-D tensors")
     B, Hq, C, D = q.shape
     Hkv = k.shape[1]
+    _tensor(q, "q", (B, Hq, C, D), torch.bfloat16, q.device)
+    _tensor(k, "k", (B, Hkv, C, D), torch.bfloat16, q.device)
+    _tensor(v, "v", (B, Hkv, C, D), torch.bfloat16, q.device)
+    cache.check_for(B, Hkv, D, q.device)
     return make_dims(B, Hq, Hkv, D, prefix_len, C, scale, prefix_lens)
-
-
-def _need(t, name, dtype=torch.bfloat16):
-    if t.dtype != dtype or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
 
 
 def fwd_workspace_bytes(dims: Dims) -> int:
@@ -178,19 +231,20 @@ def _workspace(nbytes, device):
 def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
                    o=None, lse=None, ws=None, prefix_lens=None):
     """O [B][Hq][C][D] bf16 and LSE [B][Hq][C] f32 of the chunk against the prefix."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
+    dims = _chunk_inputs(q, k, v, cache, prefix_len, scale, prefix_lens)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _tensor(o, "o", q.shape, torch.bfloat16, q.device)
+    _tensor(lse, "lse", q.shape[:3], torch.float32, q.device)
     if ws is None:
         ws = _workspace(fwd_workspace_bytes(dims), q.device)
+    nws = _ws_bytes(ws, q.device)
     cd = cache.desc()
     _check(_lib.pka_chunk_attn_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
-                                   ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws),
-                                   0 if ws is None else ws.numel(), _stream(q.device)),
+                                   ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws), nws,
+                                   _stream(q.device)),
            "pka_chunk_attn_fwd")
     return o, lse
 
@@ -198,19 +252,20 @@ def chunk_attn_fwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
 def chunk_attn_fwd_append(q, k, v, cache: PrefixCache, prefix_len: int, scale: float,
                           o=None, lse=None, ws=None, prefix_lens=None):
     """chunk_attn_fwd and the append of k, v to cache rows [P_b, P_b + C) in one launch."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
+    dims = _chunk_inputs(q, k, v, cache, prefix_len, scale, prefix_lens)
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _tensor(o, "o", q.shape, torch.bfloat16, q.device)
+    _tensor(lse, "lse", q.shape[:3], torch.float32, q.device)
     if ws is None:
         ws = _workspace(fwd_workspace_bytes(dims), q.device)
+    nws = _ws_bytes(ws, q.device)
     cd = cache.desc()
     _check(_lib.pka_chunk_attn_fwd_append(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                           ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(ws),
-                                          0 if ws is None else ws.numel(), _stream(q.device)),
+                                          nws, _stream(q.device)),
            "pka_chunk_attn_fwd_append")
     return o, lse
 
@@ -218,20 +273,26 @@ def chunk_attn_fwd_append(q, k, v, cache: PrefixCache, prefix_len: int, scale: f
 def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o, lse,
                    d_o, dq=None, dk=None, dv=None, delta=None, ws=None, prefix_lens=None):
     """dQ (chunk rows), dK and dV (the chunk's own keys); the prefix gets nothing."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (d_o, "d_o")):
-        _need(t, n)
-    _need(lse, "lse", torch.float32)
-    dims = _chunk_dims(q, k, prefix_len, scale, prefix_lens)
+    dims = _chunk_inputs(q, k, v, cache, prefix_len, scale, prefix_lens)
+    _tensor(o, "o", q.shape, torch.bfloat16, q.device)
+    _tensor(d_o, "d_o", q.shape, torch.bfloat16, q.device)
+    _tensor(lse, "lse", q.shape[:3], torch.float32, q.device)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    _tensor(dq, "dq", q.shape, torch.bfloat16, q.device)
+    _tensor(dk, "dk", k.shape, torch.bfloat16, q.device)
+    _tensor(dv, "dv", k.shape, torch.bfloat16, q.device)
+    if delta is not None:
+        _tensor(delta, "delta", q.shape[:3], torch.float32, q.device)
     if ws is None:
         ws = _workspace(bwd_workspace_bytes(dims), q.device)
+    nws = _ws_bytes(ws, q.device)
     cd = cache.desc()
     _check(_lib.pka_chunk_attn_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
                                    ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(d_o),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(ws),
-                                   0 if ws is None else ws.numel(), _stream(q.device)),
+                                   nws, _stream(q.device)),
            "pka_chunk_attn_bwd")
     return dq, dk, dv
 
@@ -245,31 +306,41 @@ def prefix_kv_grad(q, cache: PrefixCache, prefix_len: int, scale: float, lse, d_
     """dK, dV (f32 [B][Hkv][H][D]) of the last `horizon` cache rows of every window from
     the chunk queries; row h is cache row P_b - H + h (zero where P_b < H). lse is the
     forward's, delta the backward's (chunk_attn_bwd(..., delta=...))."""
-    _need(q, "q")
-    _need(d_o, "d_o")
-    _need(lse, "lse", torch.float32)
-    _need(delta, "delta", torch.float32)
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-D tensor")
     B, Hq, C, D = q.shape
     Hkv = cache.n_heads_kv
+    _tensor(q, "q", q.shape, torch.bfloat16, q.device)
+    _tensor(d_o, "d_o", q.shape, torch.bfloat16, q.device)
+    _tensor(lse, "lse", q.shape[:3], torch.float32, q.device)
+    _tensor(delta, "delta", q.shape[:3], torch.float32, q.device)
+    cache.check_for(B, Hkv, D, q.device)
+    if int(horizon) < 0:
+        raise ValueError("horizon must be >= 0")
     dims = make_dims(B, Hq, Hkv, D, prefix_len, C, scale, prefix_lens)
     shape = (B, Hkv, int(horizon), D)
     dk = torch.empty(shape, dtype=torch.float32, device=q.device) if dk is None else dk
     dv = torch.empty(shape, dtype=torch.float32, device=q.device) if dv is None else dv
+    _tensor(dk, "dk", shape, torch.float32, q.device)
+    _tensor(dv, "dv", shape, torch.float32, q.device)
     if ws is None:
         ws = _workspace(prefix_kv_grad_workspace_bytes(dims, horizon), q.device)
+    nws = _ws_bytes(ws, q.device)
     cd = cache.desc()
     _check(_lib.pka_prefix_kv_grad(ctypes.byref(dims), int(horizon), _ptr(q), ctypes.byref(cd),
                                    _ptr(lse), _ptr(d_o), _ptr(delta), _ptr(dk), _ptr(dv),
-                                   _ptr(ws), 0 if ws is None else ws.numel(),
-                                   _stream(q.device)),
+                                   _ptr(ws), nws, _stream(q.device)),
            "pka_prefix_kv_grad")
     return dk, dv
 
 
 def _append(fn, name, k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
-    _need(k, "k")
-    _need(v, "v")
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a 4-D tensor")
     B, Hkv, C, D = k.shape
+    _tensor(k, "k", k.shape, torch.bfloat16, k.device)
+    _tensor(v, "v", k.shape, torch.bfloat16, k.device)
+    cache.check_for(B, Hkv, D, k.device)
     dims = make_dims(B, Hkv, Hkv, D, prefix_len, C, 1.0, prefix_lens)
     cd = cache.desc()
     _check(fn(ctypes.byref(dims), _ptr(k), _ptr(v), ctypes.byref(cd), _stream(k.device)), name)
@@ -298,7 +369,9 @@ def kv_append(k, v, cache: PrefixCache, prefix_len: int, prefix_lens=None):
 
 def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = True):
     """(f32, bf16 or None) [2][B][Hkv][rows][D]: cache rows as the attention reads them."""
-    shape = (2, cache.batch, cache.n_heads_kv, rows, cache.head_dim)
+    if int(row0) < 0 or int(rows) < 0:
+        raise ValueError("row0 and rows must be >= 0")
+    shape = (2, cache.batch, cache.n_heads_kv, int(rows), cache.head_dim)
     out = torch.empty(shape, dtype=torch.float32, device=cache.k.device)
     outb = torch.empty(shape, dtype=torch.bfloat16, device=cache.k.device) if want_bf16 else None
     cd = cache.desc()

@@ -283,8 +283,56 @@ def test_error_paths_raise_before_launch():
     with pytest.raises(pka.PkaError, match="UNSUPPORTED"):
         pka.kv_append_q8_0(case.dev["kc"], case.dev["vc"], case.cache, 64)
     q96 = torch.zeros((1, 2, 16, 96), dtype=torch.bfloat16, device=DEV)
+    c96 = pka.PrefixCache.empty("f16", 1, 1, 80, 96, DEV)
     with pytest.raises(pka.PkaError, match="UNSUPPORTED"):
-        pka.chunk_attn_fwd(q96, q96[:, :1], q96[:, :1], case.cache, 64, 0.1)
+        pka.chunk_attn_fwd(q96, q96[:, :1].contiguous(), q96[:, :1].contiguous(), c96, 64, 0.1)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The C entry points see bare pointers: the binding checks every tensor's shape,
+    dtype, device and layout first and raises ValueError without launching."""
+    import prefix_kv_attention_amd as pka
+    w = synthetic.small("shapes", prefix_len=64, chunk_len=16, n_heads_q=4, n_heads_kv=2)
+    case = Case(w)
+    d, P, sc = case.dev, w.prefix_len, w.softmax_scale
+    q, k, v = d["q"], d["kc"], d["vc"]
+    o, lse = pka.chunk_attn_fwd(q, k, v, case.cache, P, sc)
+    torch.cuda.synchronize()
+    bad_calls = {
+        "v shorter": lambda: pka.chunk_attn_fwd(q, k, v[:, :, :8].contiguous(), case.cache, P, sc),
+        "o shape": lambda: pka.chunk_attn_fwd(q, k, v, case.cache, P, sc, o=o[:, :2].contiguous()),
+        "lse dtype": lambda: pka.chunk_attn_fwd(q, k, v, case.cache, P, sc, lse=lse.double()),
+        "q on cpu": lambda: pka.chunk_attn_fwd(q.cpu(), k, v, case.cache, P, sc),
+        "q transposed": lambda: pka.chunk_attn_fwd(q.transpose(2, 3), k, v, case.cache, P, sc),
+        "ws on cpu": lambda: pka.chunk_attn_fwd(q, k, v, case.cache, P, sc,
+                                                ws=torch.empty(1 << 20, dtype=torch.uint8)),
+        "cache batch": lambda: pka.chunk_attn_fwd(
+            q, k, v, pka.PrefixCache.empty("f16", 2, 2, P + 16, 64, DEV), P, sc),
+        "dk shape": lambda: pka.chunk_attn_bwd(q, k, v, case.cache, P, sc, o, lse, d["do"],
+                                               dk=torch.empty_like(q)),
+        "delta shape": lambda: pka.chunk_attn_bwd(
+            q, k, v, case.cache, P, sc, o, lse, d["do"],
+            delta=torch.empty(q.shape[:2], dtype=torch.float32, device=DEV)),
+        "d_o dtype": lambda: pka.chunk_attn_bwd(q, k, v, case.cache, P, sc, o, lse,
+                                                d["do"].float()),
+        "prefix dk shape": lambda: pka.prefix_kv_grad(
+            q, case.cache, P, sc, lse, d["do"], torch.zeros_like(lse), 32,
+            dk=torch.empty((1, 2, 16, 64), dtype=torch.float32, device=DEV)),
+        "append v shape": lambda: pka.kv_append(k, v[:, :1].contiguous(), case.cache, P),
+        "cache dtype": lambda: pka.PrefixCache(
+            "bf16", case.cache.k, case.cache.v),   # an f16 cache's tensors as bf16
+        "q8 scales": lambda: pka.PrefixCache(
+            "q8_0", torch.empty((1, 2, 80, 64), dtype=torch.int8, device=DEV),
+            torch.empty((1, 2, 80, 64), dtype=torch.int8, device=DEV)),
+    }
+    for name, call in bad_calls.items():
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(f"{name}: no error")
+    torch.cuda.synchronize()
+    o2, lse2 = pka.chunk_attn_fwd(q, k, v, case.cache, P, sc)   # the good call still works
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
 @pytest.mark.parametrize("ct", ["q8_0", "f16", "bf16"])
