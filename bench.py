@@ -85,8 +85,10 @@ def read_traffic(kernel_name):
         return None
 
 
-def cpu_baseline(w, inputs, budget_s=15.0):
-    """Time the fp64 oracle on (window, KV head) groups until ~budget_s is spent."""
+def cpu_baseline(w, inputs, budget_s=15.0, gpu_out=None):
+    """Time the fp64 oracle on (window, KV head) groups until ~budget_s is spent. With
+    gpu_out (host copies of the step's O, LSE, dQ, dK, dV) it also reports the GPU's
+    errors against the oracle on the groups it computed."""
     import numpy as np
     import oracle
     from oracle.cache import from_torch_bf16
@@ -98,6 +100,7 @@ def cpu_baseline(w, inputs, budget_s=15.0):
     G = w.group
     sc = w.softmax_scale
     done, spent, fl = 0, 0.0, 0.0
+    acc, lse_err = {}, 0.0
     fwd_f, bwd_f, _ = flops(w)
     per_group = (fwd_f + bwd_f) / (w.batch * w.n_heads_kv)
     groups = [(b, kv) for b in range(w.batch) for kv in range(w.n_heads_kv)]
@@ -109,18 +112,36 @@ def cpu_baseline(w, inputs, budget_s=15.0):
         q, kc, vc, do = f(inputs["q"][b, hs]), f(inputs["kc"][b, kv]), f(inputs["vc"][b, kv]), \
             f(inputs["do"][b, hs])
         t0 = time.perf_counter()
-        oracle.group_fwd(q, kc, vc, kp, vp, sc)
-        oracle.group_bwd(q, kc, vc, kp, vp, sc, do)
+        ro, rl = oracle.group_fwd(q, kc, vc, kp, vp, sc)
+        rdq, rdk, rdv, _ = oracle.group_bwd(q, kc, vc, kp, vp, sc, do)
         spent += time.perf_counter() - t0
         done += 1
         fl += per_group
+        if gpu_out is not None:
+            pairs_ = (("o", gpu_out["o"][b, hs], ro), ("dq", gpu_out["dq"][b, hs], rdq),
+                      ("dk", gpu_out["dk"][b, kv], rdk), ("dv", gpu_out["dv"][b, kv], rdv))
+            for name, got, ref in pairs_:
+                acc.setdefault(name, [[], []])
+                acc[name][0].append(f(got).ravel())
+                acc[name][1].append(ref.ravel())
+            lse_err = max(lse_err, float(np.abs(gpu_out["lse"][b, hs].double().numpy()
+                                                - rl).max()))
         if spent >= budget_s:
             break
-    return {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (window, KV head) groups of {w.name} "
-                      f"({G} query heads x {w.chunk_len} rows vs {w.prefix_len + w.chunk_len} "
-                      f"keys each), fp64 forward + backward, {spent:.1f} s"}
+    out = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+           "kind": "oracle",
+           "sample": f"{done} of {len(groups)} (window, KV head) groups of {w.name} "
+                     f"({G} query heads x {w.chunk_len} rows vs {w.prefix_len + w.chunk_len} "
+                     f"keys each), fp64 forward + backward, {spent:.1f} s"}
+    if gpu_out is not None:
+        err = {}
+        for name, (a, r) in acc.items():
+            a, r = np.concatenate(a), np.concatenate(r)
+            err[name] = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+        err["lse_abs"] = lse_err
+        out["parity_vs_gpu"] = {k: round(v, 6) for k, v in err.items()}
+        out["parity_vs_gpu"]["groups"] = done
+    return out
 
 
 def time_prefix_kv_grad(pka, w, t, cache, horizon, steps, warmup):
@@ -162,6 +183,36 @@ def time_prefix_kv_grad(pka, w, t, cache, horizon, steps, warmup):
             "reduce_ms": round(red_tot / red_n, 5) if red_n else 0.0,
             "flop_per_launch": flop, "achieved": round(flop / (ms * 1e-3) / 1e12, 2),
             "unit": "TFLOP/s", "frac": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+def _pct(xs):
+    import numpy as np
+    a = np.asarray(xs)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def time_phases(parts, n, scratch=None):
+    """ms of each part of the step (fwd, bwd, append) and of the whole step over n
+    iterations, torch events on the current stream (the one the library launches on).
+    scratch: a large device buffer rewritten before each iteration (evicts L2 and the
+    last-level cache: cold runs)."""
+    import torch
+    names = list(parts) + ["step"]
+    times = {k: [] for k in names}
+    for i in range(n):
+        if scratch is not None:
+            scratch.fill_(i & 0xFF)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+        ev[0].record()
+        for j, fn in enumerate(parts.values()):
+            fn()
+            ev[j + 1].record()
+        torch.cuda.synchronize()
+        for j, k in enumerate(parts):
+            times[k].append(ev[j].elapsed_time(ev[j + 1]))
+        times["step"].append(ev[0].elapsed_time(ev[-1]))
+    return {k: _pct(v) for k, v in times.items()}
 
 
 def time_decode(pka, w, t, cache, steps, warmup):
@@ -206,6 +257,9 @@ def main():
     ap.add_argument("--prefix-horizon", type=int, default=0,
                     help="also time pka_prefix_kv_grad (dK/dV of the last H prefix rows) "
                          "on the same inputs, outside the step")
+    ap.add_argument("--no-phases", action="store_true",
+                    help="skip the untimed warm / cold passes that time fwd, bwd and append "
+                         "separately")
     ap.add_argument("--decode", action="store_true",
                     help="also time the fused forward + cache append against the two "
                          "separate calls, outside the step")
@@ -253,10 +307,19 @@ def main():
     ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev) if wsf else None
     ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
-    def step():
+    def fwd():
         pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
+
+    def bwd():
         pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b)
+
+    def append():
         pka.kv_append(kc, vc, cache, P)
+
+    def step():
+        fwd()
+        bwd()
+        append()
 
     for _ in range(args.warmup):
         step()
@@ -324,6 +387,15 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if not args.no_phases:
+        # Untimed passes after the timed loop: the parts of the step, warm (back to back)
+        # and cold (a 1 GiB device write before each step evicts L2 and the MALL).
+        n_ph = min(args.steps, 30)
+        parts = {"fwd": fwd, "bwd": bwd, "append": append}
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        out["phases_ms"] = {"iterations": n_ph, "warm": time_phases(parts, n_ph),
+                            "cold": time_phases(parts, n_ph, scratch)}
+        del scratch
     if args.prefix_horizon > 0:
         out["prefix_kv_grad"] = time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
@@ -332,7 +404,13 @@ def main():
         out["decode"] = time_decode(pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse), cache,
                                     args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget)
+        # The step is deterministic: one more recomputes the outputs the oracle checks.
+        fwd()
+        bwd()
+        torch.cuda.synchronize()
+        gpu_out = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(),
+                   "dv": dv.cpu()}
+        out["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_budget, gpu_out)
     print(json.dumps(out), flush=True)
 
 
