@@ -215,6 +215,29 @@ def time_phases(parts, n, scratch=None):
     return {k: _pct(v) for k, v in times.items()}
 
 
+def time_graph(step, steps, warmup):
+    """ms per step replayed from a HIP graph of one captured step (the library makes
+    no allocation, memset or sync inside its calls), after `warmup` replays."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return round((time.perf_counter() - t0) * 1e3 / steps, 5)
+
+
 def time_decode(pka, w, t, cache, steps, warmup):
     """Time the re-decode of a chunk into the cache two ways: one fused launch
     (pka_chunk_attn_fwd_append) against pka_chunk_attn_fwd followed by
@@ -260,6 +283,8 @@ def main():
     ap.add_argument("--no-phases", action="store_true",
                     help="skip the untimed warm / cold passes that time fwd, bwd and append "
                          "separately")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph")
     ap.add_argument("--decode", action="store_true",
                     help="also time the fused forward + cache append against the two "
                          "separate calls, outside the step")
@@ -396,6 +421,10 @@ def main():
         out["phases_ms"] = {"iterations": n_ph, "warm": time_phases(parts, n_ph),
                             "cold": time_phases(parts, n_ph, scratch)}
         del scratch
+    if args.graph:
+        g_ms = time_graph(step, args.steps, args.warmup)
+        out["graph"] = {"ms_per_step": g_ms, "value": round((fwd_f + bwd_f) / (g_ms * 1e-3)
+                                                            / 1e12, 2)}
     if args.prefix_horizon > 0:
         out["prefix_kv_grad"] = time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
