@@ -53,6 +53,11 @@ EDGE = [
     # row split of dK/dV without a prefix split of dQ (256 dQ units, 64 dK/dV units)
     synthetic.small("dkv-split-only", batch=8, prefix_len=128, chunk_len=64, n_heads_q=128,
                     n_heads_kv=8, head_dim=64, cache_type="f16", qkv_std=0.3, prefix_std=0.3),
+    # very sharp softmax (logit std ~9 and ~4): the forward raises its reference max
+    # often and most probabilities underflow
+    synthetic.small("very-sharp-bf16", prefix_len=1000, chunk_len=130, n_heads_q=4,
+                    n_heads_kv=1, head_dim=128, cache_type="bf16", qkv_std=3.0,
+                    prefix_std=3.0),
     # plain causal attention over a long chunk: every tile crosses the chunk
     synthetic.small("p0-c2048", batch=1, prefix_len=0, chunk_len=2048, n_heads_q=4,
                     n_heads_kv=2, head_dim=128, cache_type="bf16", qkv_std=0.3),
@@ -190,6 +195,41 @@ def test_dequant_hook_bitexact():
         np.testing.assert_array_equal(f32[i].cpu().numpy(), ref)
         np.testing.assert_array_equal(
             bf[i].cpu().view(torch.int16).numpy().view(np.uint16), oracle.f32_to_bf16_rne(ref))
+
+
+def test_very_sharp_q8_lse_within_operand_rounding_bound():
+    """Large keys from a q8_0 cache (2 % outliers x8 at std 2: |k| up to ~50) and a
+    sharp softmax. The MFMA reads each dequantised key rounded to bf16 (relative error
+    <= 2^-8), so a score moves by at most scale * 2^-8 * sum_d |q_d k_d|; LSE is
+    1-Lipschitz in the scores (sup norm), and the row sum of bf16 probabilities adds
+    <= 2^-8 relative. Each row's LSE error must stay within that bound (the fixed 5e-3
+    bar assumes unit-scale logits); O, dQ, dK, dV keep the standard bars."""
+    w = synthetic.small("very-sharp-q8", batch=2, prefix_len=700, chunk_len=70, n_heads_q=6,
+                        n_heads_kv=2, head_dim=64, cache_type="q8_0", qkv_std=2.0,
+                        prefix_std=2.0, outlier_frac=0.02)
+    print(_label(w), flush=True)
+    case = Case(w)
+    o, lse = case.fwd()
+    dq, dk, dv = case.bwd(o, lse)
+    torch.cuda.synchronize()
+    groups = case.all_groups()
+    errs = compare_groups(case, groups, o, lse, dq, dk, dv)
+    print(errs, flush=True)
+    assert_within({k: v for k, v in errs.items() if k != "lse_abs"}, _label(w))
+    kpv, _ = case.oracle_prefix()
+    G, P = w.group, w.prefix_len
+    worst = 0.0
+    for b, kv in groups:
+        hs = slice(kv * G, (kv + 1) * G)
+        q = np.abs(f64(case.cpu["q"][b, hs]))                           # [G][C][D]
+        kf = np.abs(np.concatenate([kpv[b, kv], f64(case.cpu["kc"][b, kv])]))
+        allowed = oracle.allowed_mask(P, w.chunk_len)                   # [C][P+C]
+        mag = np.where(allowed[None], q @ kf.T, 0.0).max(axis=2)         # [G][C]
+        bound = w.softmax_scale * 2.0 ** -8 * mag + 2.0 ** -8 + 1e-4
+        err = np.abs(f64(lse[b, hs]) - case.oracle_group(b, kv)["lse"])
+        assert np.all(err <= bound), f"(b={b}, kv={kv}): LSE error above its bound"
+        worst = max(worst, float((err / bound).max()))
+    print(f"largest LSE error / bound: {worst:.3f}", flush=True)
 
 
 def test_closed_form_zero_queries():
