@@ -27,8 +27,11 @@
 //                serves 128 keys, halving the query-row re-reads of 64-key blocks.
 //                The sum over the G heads of a KV head falls out of the packing.
 //                When (window, KV head, key block) units are few, each is split
-//                over disjoint query-row ranges whose fp32 partials
+//                over disjoint query-row ranges (a key block gets splits in
+//                proportion to the rows that see it) whose fp32 partials
 //                bwd_reduce sums in a fixed order (one launch with the dQ sums).
+//  Separately, pka_prefix_kv_grad runs the same dK/dV kernel over the last H cache
+//  rows of each window (every chunk row sees them), with fp32 outputs.
 // No atomics anywhere: every output element is owned by one lane (deterministic).
 #include "pka_device.hpp"
 

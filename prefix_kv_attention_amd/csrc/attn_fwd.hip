@@ -22,10 +22,17 @@
 //    a fast path (uniform base pointer, fixed per-thread offsets); F16 / q8_0 rows
 //    are converted to bf16 while staging (dequantised on load). Only tiles that
 //    cross the causal diagonal are masked.
-//  * The running max is raised only when a row's tile max exceeds it by more than
-//    8 (in log2 units), so the rescale of the accumulator is skipped on almost every
-//    tile; probabilities then stay below 2^8, which bf16 and fp32 hold exactly
-//    enough. The result is the same softmax (any reference max gives it).
+//  * The probabilities of a tile are taken against the running reference max; the
+//    reference is raised to the exact row max (and the accumulator rescaled) only
+//    when it is unset or a lane's partial row sum of the tile exceeds 2^8, which any
+//    probability above 2^8 forces. So the max reduction and the rescale are skipped
+//    on almost every tile, and probabilities stay <= 2^8, which bf16 and fp32 hold
+//    exactly enough. The result is the same softmax (any reference max gives it).
+//  * LDS operand reads run several MFMAs ahead of their use (sched_ahead), the two
+//    32-key S chains of a tile interleave, and the first P V operands are read before
+//    the softmax: without that the wave waits out the LDS latency at each MFMA.
+//  * With FwdParams::append the same launch writes the chunk's K/V into the cache
+//    rows [P_b, P_b + C) after its last tile (the re-decode into the cache).
 //  * When (window, KV head, row block) units are too few to fill 256 CUs, the key
 //    tiles are split over several workgroups; partial (O, LSE) are merged by
 //    fwd_combine in a fixed order (deterministic).
