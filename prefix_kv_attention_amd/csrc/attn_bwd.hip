@@ -22,9 +22,11 @@
 //                query rows of all G heads that can see them (token >= key) in tiles
 //                of 64: S = Q K^T and dP = dO V^T with keys as MFMA columns, then
 //                dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposing reads).
-//                Each of the 4 waves owns 32 keys and takes both 32-row halves of
-//                every tile (four independent MFMA chains per wave); a staged tile
-//                serves 128 keys, halving the query-row re-reads of 64-key blocks.
+//                8 waves, two per SIMD: wave w owns 32 keys (w % 4) and one 32-row
+//                half (w / 4) of every tile; the 128 keys' K / V rows stay in LDS
+//                as MFMA operands, and a staged tile serves all 128 keys (half the
+//                query-row re-reads of 64-key blocks). The two halves' sums meet in
+//                LDS at the end.
 //                The sum over the G heads of a KV head falls out of the packing.
 //                When (window, KV head, key block) units are few, each is split
 //                over disjoint query-row ranges (a key block gets splits in
@@ -234,12 +236,21 @@ constexpr int KB = kDkvKeysPerBlock;        // keys per dK/dV workgroup (128)
 template <int D>
 struct DkvLds {
   static constexpr int S = D + 8;
-  uint16_t q[2][BQ * S];
-  uint16_t g[2][BQ * S];   // dO
+  union {
+    struct {
+      uint16_t q[2][BQ * S];
+      uint16_t g[2][BQ * S];   // dO
+      uint16_t k[KB * S];      // the workgroup's keys, row-major (rows permuted by prow)
+      uint16_t v[KB * S];
+    } t;
+    float red[4][32 * D * 2];  // dK^T, dV^T partial sums of the waves of row half 1
+  } u;
   __align__(16) float lse2[2][BQ];
   __align__(16) float dlt[2][BQ];   // -delta of the staged rows
   __align__(16) int tok[2][BQ];
 };
+
+constexpr int NTHR_KV = 512;   // 8 waves: 4 key blocks of 32 x 2 row halves
 
 // dK/dV of one block of 128 keys of one (window, KV head), over the packed query
 // rows of all G heads that see them. PREFIX = false: the chunk's own keys (causal:
@@ -248,20 +259,26 @@ struct DkvLds {
 // chunk row sees them), dequantised on load like the forward; fp32 outputs
 // dkp, dvp [B][Hkv][H][D] whose row h is cache row P_b - H + h (zero when that row
 // does not exist because P_b < H).
+// Wave w owns keys kw*32 .. kw*32+31 (kw = w % 4) and row half qb = w / 4 of every
+// step of 64 rows; two waves per SIMD. The keys' K / V rows sit in LDS for the whole
+// launch (the B operands of S and dP); the two row halves' sums meet in LDS at the end.
 template <int D, int CT, bool PREFIX>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
   __shared__ __align__(16) DkvLds<D> sm;
   constexpr int S = DkvLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int NT = (BQ / 4) * CH;   // staging tasks per tensor (<= 256)
-  static_assert(KB == 32 * 4, "one block of 32 keys per wave");
+  constexpr int RT = 2 * BQ * CH / NTHR_KV;   // rows a thread stages per step (4 or 2)
+  constexpr int NT = (BQ / RT) * CH;          // staging tasks per tensor (one per thread)
+  static_assert(KB == 32 * 4, "four key blocks of 32");
+  static_assert(2 * NT == NTHR_KV, "one staging task per thread");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int kw = wave;           // key block of this wave
+  const int kw = wave & 3;       // key block of this wave
+  const int qb = wave >> 2;      // row half of every step this wave takes
   const int C = (int)p.C;
   const int G = p.G;
   const int rows = G * C;
@@ -288,45 +305,42 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   }
   const int b = grp / p.Hkv, kv = grp % p.Hkv;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
+  const int key = kblk * KB + kw * 32 + l32;  // key index of this launch (output row)
+  const int64_t Pb = PREFIX ? window_prefix(p.plens, b, p.P) : 0;
+  // A prefix row that does not exist (P_b < H) contributes and gets exactly zero.
+  const bool key_ok = key < NK && (!PREFIX || Pb - NK + key >= 0);
 
-  const int key = kblk * KB + kw * 32 + l32;  // key index of this launch
-  bool key_ok = key < NK;
-  bf16x8 kreg[NKS], vreg[NKS];
-  if constexpr (PREFIX) {
-    const int64_t Pb = window_prefix(p.plens, b, p.P);
-    const int64_t j = Pb - NK + key;           // cache row
-    key_ok = key_ok && j >= 0;
+  // The workgroup's 128 K and V rows into LDS (8 rows-of-8 per thread), converted to
+  // bf16; missing keys are zero rows.
+  {
     constexpr int ESZ = (CT == kQ8) ? 1 : 2;
     const char* ck = static_cast<const char*>(p.cache.k) + bh * p.cache.cap * D * ESZ;
     const char* cv = static_cast<const char*>(p.cache.v) + bh * p.cache.cap * D * ESZ;
     const uint16_t* cks = (CT == kQ8) ? p.cache.ks + bh * p.cache.cap * (D / 32) : nullptr;
     const uint16_t* cvs = (CT == kQ8) ? p.cache.vs + bh * p.cache.cap * (D / 32) : nullptr;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (key_ok) {
-        RawRow8 rk, rv;
-        load_row8<CT, D>(rk, ck, cks, nullptr, Pb, 0, j, ks * 16 + hf * 8);
-        load_row8<CT, D>(rv, cv, cvs, nullptr, Pb, 0, j, ks * 16 + hf * 8);
-        kreg[ks] = __builtin_bit_cast(bf16x8, to_bf16x8<CT>(rk, true));
-        vreg[ks] = __builtin_bit_cast(bf16x8, to_bf16x8<CT>(rv, true));
+    for (int it = 0; it < (2 * KB * CH) / NTHR_KV; ++it) {
+      const int task = it * NTHR_KV + tid;
+      const bool is_v = task >= KB * CH;
+      const int tk = is_v ? task - KB * CH : task;
+      const int kr = tk / CH, d0 = (tk % CH) * 8;
+      const int kk = kblk * KB + kr;       // key index of the row
+      u32x4 w = u32x4{0u, 0u, 0u, 0u};
+      if constexpr (PREFIX) {
+        const int64_t j = Pb - NK + kk;    // cache row
+        if (kk < NK && j >= 0) {
+          RawRow8 r;
+          load_row8<CT, D>(r, is_v ? cv : ck, is_v ? cvs : cks, nullptr, Pb, 0, j, d0);
+          w = to_bf16x8<CT>(r, true);
+        }
       } else {
-        kreg[ks] = bf16x8{};
-        vreg[ks] = bf16x8{};
+        if (kk < NK)
+          w = *reinterpret_cast<const u32x4*>((is_v ? p.vc : p.kc) + (bh * C + kk) * D + d0);
       }
-    }
-  } else {
-    const uint16_t* kp = p.kc + (bh * C + (key_ok ? key : 0)) * D + hf * 8;
-    const uint16_t* vp = p.vc + (bh * C + (key_ok ? key : 0)) * D + hf * 8;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kreg[ks] = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
-      vreg[ks] = *reinterpret_cast<const bf16x8*>(vp + ks * 16);
-      if (!key_ok) {
-        kreg[ks] = bf16x8{};
-        vreg[ks] = bf16x8{};
-      }
+      *reinterpret_cast<u32x4*>(&(is_v ? sm.u.t.v : sm.u.t.k)[prow(kr) * S + d0]) = w;
     }
   }
+
   f32x16 acck[NDB], accv[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
@@ -342,18 +356,20 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int s_hi = (int)((int64_t)(rsplit + 1) * steps_unit / RSk);
   const int r_begin = r_unit + s_lo * BQ;   // this split's rows
   const int n_steps = s_hi - s_lo;
-  const bool stager = tid < NT;
-  const int tr0 = (tid / CH) * 4, td0 = (tid % CH) * 8;
+  const bool is_g = tid >= NT;             // stages dO rows (else Q rows)
+  const int ts = is_g ? tid - NT : tid;
+  const int tr0 = (ts / CH) * RT, td0 = (ts % CH) * 8;
+  const uint16_t* src_base = is_g ? p.d_o : p.q;
 
   // Packed row rr is token rr / G of query head kv*G + rr % G. Each thread follows
   // its rows from step to step (+BQ rows per step) without dividing.
   const int dt_step = BQ / G, dg_step = BQ % G;
   const int64_t head0 = (int64_t)b * p.Hq + kv * G;   // first query head of this KV head
-  int tq[4], gq[4];       // (token, head-in-group) of the 4 staged rows
+  int tq[RT], gq[RT];     // (token, head-in-group) of the staged rows
   int tl = 0, gl = 0;     // same for the row whose LSE / delta this thread stages
   {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RT; ++i) {
       const int rr = r_begin + tr0 + i;
       tq[i] = rr / G;
       gq[i] = rr - tq[i] * G;
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
       t += 1;
     }
   };
-  u32x4 rq[4], rg[4];
+  u32x4 rq[RT];
   float pl = 0.f, pd = 0.f;   // raw LSE and delta of the staged row: they are scaled
   int ptok = -1;              // when written to LDS, a step after their loads
   int rows_left = 0;          // rows of the issued step that exist (>= BQ: all)
@@ -391,116 +407,97 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     // Rows past the last one (only in the last step) load a valid row and are zeroed
     // when staged: no register is written here but by the loads themselves.
     rows_left = rows - r0;
-    if (stager) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = tr0 + i < rows_left;
-        const int64_t row = ok ? (head0 + gq[i]) * C + tq[i] : head0 * C;
-        rq[i] = *reinterpret_cast<const u32x4*>(p.q + row * D + td0);
-        rg[i] = *reinterpret_cast<const u32x4*>(p.d_o + row * D + td0);
-        advance(tq[i], gq[i]);
-      }
+    for (int i = 0; i < RT; ++i) {
+      const bool ok = tr0 + i < rows_left;
+      const int64_t row = ok ? (head0 + gq[i]) * C + tq[i] : head0 * C;
+      rq[i] = *reinterpret_cast<const u32x4*>(src_base + row * D + td0);
+      advance(tq[i], gq[i]);
     }
   };
   auto stage = [&](int buf) {
-    if (stager) {
-      if (rows_left < BQ) {   // the last step: zero the rows past the end
+    if (rows_left < BQ) {   // the last step: zero the rows past the end
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (tr0 + i >= rows_left) {
-            rq[i] = u32x4{0u, 0u, 0u, 0u};
-            rg[i] = u32x4{0u, 0u, 0u, 0u};
-          }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<u32x4*>(&sm.q[buf][prow(tr0 + i) * S + td0]) = rq[i];
-        *reinterpret_cast<u32x4*>(&sm.g[buf][prow(tr0 + i) * S + td0]) = rg[i];
-      }
+      for (int i = 0; i < RT; ++i)
+        if (tr0 + i >= rows_left) rq[i] = u32x4{0u, 0u, 0u, 0u};
     }
+    uint16_t* dst = is_g ? sm.u.t.g[buf] : sm.u.t.q[buf];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+      *reinterpret_cast<u32x4*>(&dst[prow(tr0 + i) * S + td0]) = rq[i];
     if (tid < BQ) {
       const bool valid = ptok >= 0;
       sm.lse2[buf][tid] = valid ? pl * kLog2e : 0.f;
-      sm.dlt[buf][tid] = valid ? -pd : 0.f;   // negated: the dP^T chain starts from it
+      sm.dlt[buf][tid] = valid ? -pd : 0.f;   // negated: the dP chain starts from it
       sm.tok[buf][tid] = ptok;
     }
   };
 
-  const int a_off = prow(l32) * S + hf * 8;   // + sb * 32 * S: row half sb of a step
+  const int a_off = (qb * 32 + prow(l32)) * S + hf * 8;   // this wave's rows of a step
+  const int k_off = (kw * 32 + prow(l32)) * S + hf * 8;   // this wave's keys
   const TrOffsets t_off = tr_lane_offsets<S>(lane);
 
   if (n_steps > 0) {
     issue(0);
     stage(0);
     if (n_steps > 1) issue(1);
-    __syncthreads();
   }
-  // One wait for every load so far (K / V rows, step 1's rows): otherwise the
-  // compiler waits at the loop top on each iteration, and that wait also covers the
-  // rows just requested for two steps ahead.
+  __syncthreads();   // the K / V rows and step 0's rows are in LDS
+  // One wait for every load so far (step 1's rows): otherwise the compiler waits at
+  // the loop top on each iteration, and that wait also covers the rows just requested
+  // for two steps ahead.
   wait_global_loads();
   // Packed rows from clean_from on have tokens >= the block's last key: no mask.
   const int clean_from = (kblk * KB + KB - 1) * G;
   for (int step = 0; step < n_steps; ++step) {
     const int cur = step & 1;
-    const uint16_t* qt = sm.q[cur];
-    const uint16_t* gt = sm.g[cur];
+    const uint16_t* qt = sm.u.t.q[cur];
+    const uint16_t* gt = sm.u.t.g[cur];
     const bool diag = !PREFIX && r_begin + step * BQ < clean_from;
-    // Both 32-row halves of the step against this wave's 32 keys: four independent
-    // MFMA chains. dP (rows x keys) starts from -delta of its rows, so the chain
-    // yields dP - delta; register i of a result is row (i / 4) * 8 + hf * 4 + i % 4 of
-    // its half.
-    f32x16 s[2], dp[2];
+    // S and dP (rows x keys) of this wave's 32 rows and 32 keys; dP starts from
+    // -delta of its rows, so the chain yields dP - delta. Register i of a result is
+    // row (i / 4) * 8 + hf * 4 + i % 4 of the half, key l32.
+    f32x16 sv = f32x16{}, dp;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      s[sb] = f32x16{};
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qb * 32 + g4 * 8 + hf * 4]);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][sb * 32 + g4 * 8 + hf * 4]);
+      for (int j = 0; j < 4; ++j) dp[g4 * 4 + j] = d4[j];
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dp[sb][g4 * 4 + j] = d4[j];
+    for (int ks = 0; ks < NKS; ++ks) {
+      sv = mfma32(*reinterpret_cast<const bf16x8*>(&qt[a_off + ks * 16]),
+                  *reinterpret_cast<const bf16x8*>(&sm.u.t.k[k_off + ks * 16]), sv);
+      dp = mfma32(*reinterpret_cast<const bf16x8*>(&gt[a_off + ks * 16]),
+                  *reinterpret_cast<const bf16x8*>(&sm.u.t.v[k_off + ks * 16]), dp);
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      // result rows (g4*8 + hf*4 + 0..3) of the half: one 16-byte read per array
+      const int q0 = qb * 32 + g4 * 8 + hf * 4;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+      const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
+      const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = g4 * 4 + j;
+        const float e = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -l4[j]));
+        // Prefix keys are seen by every row; padding rows past the last one have
+        // zero q and dO and so add nothing. Chunk keys: causal, checked only in
+        // the steps that reach below the block's last key.
+        const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
+        pb[i >> 3][i & 7] = (__bf16)pv;
+        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int o = a_off + sb * 32 * S + ks * 16;
-        s[sb] = mfma32(*reinterpret_cast<const bf16x8*>(&qt[o]), kreg[ks], s[sb]);
-        dp[sb] = mfma32(*reinterpret_cast<const bf16x8*>(&gt[o]), vreg[ks], dp[sb]);
-      }
-    bf16x8 pb[2][2], dsb[2][2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // result rows (g4*8 + hf*4 + 0..3) of row half sb: one 16-byte read per
-        // per-row array
-        const int q0 = sb * 32 + g4 * 8 + hf * 4;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
-        const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
-        const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = g4 * 4 + j;
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[sb][i], c, -l4[j]));
-          // Prefix keys are seen by every row; padding rows past the last one have
-          // zero q and dO and so add nothing. Chunk keys: causal, checked only in
-          // the steps that reach below the block's last key.
-          const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
-          pb[sb][i >> 3][i & 7] = (__bf16)pv;
-          dsb[sb][i >> 3][i & 7] = (__bf16)(pv * dp[sb][i]);
-        }
-      }
-#pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int ss = 0; ss < 2; ++ss) {
-          accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, sb * 32 + ss * 16, db * 32), pb[sb][ss], accv[db]);
-          acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, sb * 32 + ss * 16, db * 32), dsb[sb][ss], acck[db]);
-        }
+      for (int ss = 0; ss < 2; ++ss) {
+        accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, qb * 32 + ss * 16, db * 32), pb[ss], accv[db]);
+        acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, qb * 32 + ss * 16, db * 32), dsb[ss], acck[db]);
+      }
     if (step + 1 < n_steps) {
       stage(cur ^ 1);
       if (step + 2 < n_steps) issue(step + 2);
@@ -508,15 +505,27 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     __syncthreads();
   }
 
-  if (key >= NK) return;
-  // A prefix row that does not exist (P_b < H) gets an exact zero.
-  if (!key_ok) {
+  // The waves of row half 1 hand their sums to those of half 0 through LDS (fp32, a
+  // fixed order); the LDS tiles are no longer read after the loop's last barrier.
+  float* red = sm.u.red[kw];
+  if (qb == 1) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      acck[db] = f32x16{};
-      accv[db] = f32x16{};
-    }
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        red[(db * 16 + i) * 64 + lane] = acck[db][i];
+        red[32 * D + (db * 16 + i) * 64 + lane] = accv[db][i];
+      }
   }
+  __syncthreads();
+  if (qb == 1 || key >= NK) return;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      acck[db][i] = key_ok ? acck[db][i] + red[(db * 16 + i) * 64 + lane] : 0.f;
+      accv[db][i] = key_ok ? accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane] : 0.f;
+    }
   const float sc = p.scale;
   if (PREFIX && RS == 1) {
     float* pk = p.dkp + (bh * NK + key) * D;
@@ -644,7 +653,7 @@ hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   const int per_grp = p.plan.dkv_nkb > 0 ? p.plan.dkv_first[nkb] : nkb * p.plan.n_dkv_split;
   prof_begin(PKA_KERNEL_BWD_DKDV, s);
   hipLaunchKernelGGL((bwd_kv_kernel<D, kBF16, false>), dim3(p.B * p.Hkv * per_grp),
-                     dim3(256), 0, s, p);
+                     dim3(NTHR_KV), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DKDV, s);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
@@ -667,7 +676,7 @@ hipError_t launch_prefix_kv_t(const BwdParams& p, hipStream_t s) {
   const int nkb = (int)((p.horizon + KB - 1) / KB);
   prof_begin(PKA_KERNEL_PREFIX_KV, s);
   hipLaunchKernelGGL((bwd_kv_kernel<D, CT, true>),
-                     dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split), dim3(256), 0, s, p);
+                     dim3(p.B * p.Hkv * nkb * p.plan.n_dkv_split), dim3(NTHR_KV), 0, s, p);
   prof_end(PKA_KERNEL_PREFIX_KV, s);
   if ((e = hipGetLastError()) != hipSuccess || p.plan.n_dkv_split == 1) return e;
   const int64_t n_dkv = 2 * (int64_t)p.B * p.Hkv * p.horizon * (D / 8);
