@@ -11,6 +11,11 @@ prefix pairs and 5 over chunk pairs; S recompute counted, avoided prefix dK/dV
 not). `roofline` is for the dominant kernel (bwd_dq), timed live with HIP events
 around each of its launches inside the timed region. `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
+
+Warm-up: the --warmup steps, then more untimed steps until --warmup-ms (250) has
+passed. From idle, the GPU's clocks take some tens of ms of load to settle (a
+kernel trace shows the forward at 650 us early on and 456 us from ~50 ms on), so a
+short warm-up would time the ramp instead of the steady state.
 """
 from __future__ import annotations
 
@@ -267,11 +272,33 @@ def time_decode(pka, w, t, cache, steps, warmup):
     return res
 
 
+def warm_up(step, n_min, ms_min):
+    """At least n_min untimed steps, continued until ms_min of wall time has passed
+    (checked at a synchronisation every 8 steps, so the time is the GPU's, not the
+    launch queue's). Returns (steps run, milliseconds)."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        if n >= n_min and (n % 8 == 0 or n_min == n):
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= ms_min:
+                break
+        step()
+        n += 1
+    return n, round((time.perf_counter() - t0) * 1e3, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-ms", type=float, default=250.0,
+                    help="after the --warmup steps, keep running untimed steps until this "
+                         "much time has passed since the warm-up began: under load the "
+                         "GPU's clocks take tens of ms to settle, and a step timed before "
+                         "that runs up to 25 %% slower")
     ap.add_argument("--workload", default="8b-16k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -346,9 +373,7 @@ def main():
         bwd()
         append()
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm = warm_up(step, args.warmup, args.warmup_ms)
 
     # Inside the timed loop only the dominant kernel (bwd_dq) is bracketed by HIP
     # events (two per step); the per-kernel breakdown comes from a short untimed
@@ -399,7 +424,8 @@ def main():
                     "launches_timed": dq_timed[1]}
     out = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm[0],
+        "warmup_ms": warm[1], "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_heads_q": Hq, "n_heads_kv": Hkv,

@@ -202,8 +202,8 @@ const char* pka_status_string(pka_status status);
 const char* pka_last_error(void);
 
 /* Opt-in kernel timing for benchmarks. When enabled, each launch of a selected
- * kernel is bracketed by two HIP events recorded on the call's stream;
- * pka_profile_read synchronises on those events and returns the summed elapsed
+ * kernel is bracketed by two HIP events recorded on the call's stream (timing-only
+ * events, created without the system-scope memory fence); pka_profile_read synchronises on those events and returns the summed elapsed
  * milliseconds and the number of launches of one kernel since the last reset. At
  * most 65536 launches per kernel are recorded between resets (later ones are
  * counted in `dropped`). pka_profile_select limits the bracketing to the kernels
