@@ -1,9 +1,10 @@
 """Benchmark of the prefix-KV chunk attention hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-chunk_attn_fwd, chunk_attn_bwd (delta, dQ, chunk-only dK/dV) and the append of the
-chunk's K/V to the cache, on the 8B-like workload by default (4 windows, 32 query /
-8 KV heads, head_dim 128, bf16 prefix cache, P = 16384, C = 512).
+chunk_attn_fwd_append (the forward and the append of the chunk's K/V to the cache,
+one launch) and chunk_attn_bwd (delta, dQ, chunk-only dK/dV), on the 8B-like
+workload by default (4 windows, 32 query / 8 KV heads, head_dim 128, bf16 prefix
+cache, P = 16384, C = 512).
 
 Prints one JSON line. `value` is fwd+bwd algorithmic TFLOP/s of the whole step
 (forward: 2 contractions over every allowed (query, key) pair; backward: 3 over
@@ -198,7 +199,7 @@ def _pct(xs):
 
 
 def time_phases(parts, n, scratch=None):
-    """ms of each part of the step (fwd, bwd, append) and of the whole step over n
+    """ms of each part of the step (fwd_append, bwd) and of the whole step over n
     iterations, torch events on the current stream (the one the library launches on).
     scratch: a large device buffer rewritten before each iteration (evicts L2 and the
     last-level cache: cold runs)."""
@@ -308,7 +309,7 @@ def main():
                     help="also time pka_prefix_kv_grad (dK/dV of the last H prefix rows) "
                          "on the same inputs, outside the step")
     ap.add_argument("--no-phases", action="store_true",
-                    help="skip the untimed warm / cold passes that time fwd, bwd and append "
+                    help="skip the untimed warm / cold passes that time fwd_append and bwd "
                          "separately")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph")
@@ -359,19 +360,18 @@ def main():
     ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev) if wsf else None
     ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
 
-    def fwd():
-        pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
+    # The forward and the append of the chunk's K/V to cache rows [P, P + C) run as one
+    # launch (pka_chunk_attn_fwd_append): the backward reads cache rows [0, P) only, so
+    # the step's outputs are those of forward, backward, then append.
+    def fwd_append():
+        pka.chunk_attn_fwd_append(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
 
     def bwd():
         pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b)
 
-    def append():
-        pka.kv_append(kc, vc, cache, P)
-
     def step():
-        fwd()
+        fwd_append()
         bwd()
-        append()
 
     warm = warm_up(step, args.warmup, args.warmup_ms)
 
@@ -430,7 +430,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_heads_q": Hq, "n_heads_kv": Hkv,
                    "head_dim": D, "prefix_len": P, "chunk_len": C, "cache": w.cache_type,
-                   "step": "chunk_attn_fwd + chunk_attn_bwd + kv_append"},
+                   "step": "chunk_attn_fwd_append + chunk_attn_bwd"},
         "prefix_kv_gbs": round(prefix_gbs, 1),
         "prefix_kv_hbm_frac": round(prefix_gbs / PEAK_HBM_GBS, 4),
         "mfma_frac_step": round(tflops / PEAK_BF16_TFLOPS, 4),
@@ -442,7 +442,7 @@ def main():
         # Untimed passes after the timed loop: the parts of the step, warm (back to back)
         # and cold (a 1 GiB device write before each step evicts L2 and the MALL).
         n_ph = min(args.steps, 30)
-        parts = {"fwd": fwd, "bwd": bwd, "append": append}
+        parts = {"fwd_append": fwd_append, "bwd": bwd}
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         out["phases_ms"] = {"iterations": n_ph, "warm": time_phases(parts, n_ph),
                             "cold": time_phases(parts, n_ph, scratch)}
@@ -460,7 +460,7 @@ def main():
                                     args.steps, args.warmup)
     if not args.no_cpu_baseline:
         # The step is deterministic: one more recomputes the outputs the oracle checks.
-        fwd()
+        fwd_append()
         bwd()
         torch.cuda.synchronize()
         gpu_out = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(),
