@@ -13,6 +13,10 @@ not). `roofline` is for the dominant kernel (bwd_dq), timed live with HIP events
 around each of its launches inside the timed region. `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
 
+--row-sparse FRAC adds the row-sparse linear backward of the projections next to
+attention ("stop-gradient through context tokens", Mechanism) for one 1.7B-class
+layer at 2048 tokens, outside the step (object `row_sparse`).
+
 Warm-up: the --warmup steps, then more untimed steps until --warmup-ms (250) has
 passed. From idle, the GPU's clocks take some tens of ms of load to settle (a
 kernel trace shows the forward at 650 us early on and 456 us from ~50 ms on), so a
@@ -191,6 +195,95 @@ def time_prefix_kv_grad(pka, w, t, cache, horizon, steps, warmup):
             "unit": "TFLOP/s", "frac": round(flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def time_row_sparse(pka, frac, steps, warmup, n_rows=2048, seed=11):
+    """Row-sparse linear backward of one decoder layer's projections ("stop-gradient
+    through context tokens", Mechanism and its microbenchmark: a 1.7B dense model at
+    sequence length 2048): q, o (2048 -> 2048), gate, up (2048 -> 6144) and down
+    (6144 -> 2048), with round(frac * 2048) kept rows in reply spans. Kernel times
+    from HIP events around each launch; work 2 * K * in * out FLOP for dW and the same
+    for dX. Also timed, as context: the same two products with torch on the GPU
+    (index_select of the kept rows, two hipBLASLt matmuls, zero and index_copy of
+    dX), and the fp64 oracle on the host for q_proj."""
+    import numpy as np
+    import torch
+    import oracle
+    import synthetic
+    dev = "cuda:0"
+    out = {"n_rows": n_rows, "keep_frac": frac, "projections": {}}
+    tot_k = tot_t = 0.0
+    tot_f = 0
+    for proj in synthetic.LAYER_1_7B:
+        inp = synthetic.row_sparse_inputs(n_rows, proj.in_features, proj.out_features, frac,
+                                          seed)
+        x, w, dy, keep = (inp[k].to(dev) for k in ("x", "w", "dy", "keep"))
+        dw = torch.empty((proj.out_features, proj.in_features), dtype=torch.float32,
+                         device=dev)
+        dx = torch.empty_like(x)
+        K = keep.numel()
+
+        def run():
+            pka.row_sparse_linear_bwd(x, w, dy, keep, dw=dw, dx=dx)
+
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        pka.profile_reset()
+        pka.profile_select(["rs_zero", "rs_dx", "rs_dw"])
+        pka.profile_enable(True)
+        for _ in range(steps):
+            run()
+        torch.cuda.synchronize()
+        pka.profile_enable(False)
+        t = {k: pka.profile_read(k)[0] / steps for k in ("rs_zero", "rs_dx", "rs_dw")}
+        kl = keep.long()
+
+        def ref():
+            xk, dyk = x.index_select(0, kl), dy.index_select(0, kl)
+            torch.matmul(dyk.t(), xk)
+            dx.zero_()
+            dx.index_copy_(0, kl, torch.matmul(dyk, w))
+
+        for _ in range(warmup):
+            ref()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(steps):
+            ref()
+        ev[1].record()
+        torch.cuda.synchronize()
+        t_ref = ev[0].elapsed_time(ev[1]) / steps
+        f = 2 * K * proj.in_features * proj.out_features
+        k_ms = t["rs_zero"] + t["rs_dx"] + t["rs_dw"]
+        tot_k += k_ms
+        tot_t += t_ref
+        tot_f += 2 * f
+        out["projections"][proj.name] = {
+            "in": proj.in_features, "out": proj.out_features, "n_keep": K,
+            "zero_ms": round(t["rs_zero"], 5), "dx_ms": round(t["rs_dx"], 5),
+            "dw_ms": round(t["rs_dw"], 5),
+            "dx_tflops": round(f / (t["rs_dx"] * 1e-3) / 1e12, 1),
+            "dw_tflops": round(f / (t["rs_dw"] * 1e-3) / 1e12, 1),
+            "torch_ms": round(t_ref, 5)}
+    out["layer_kernel_ms"] = round(tot_k, 5)
+    out["flop"] = tot_f
+    out["achieved"] = round(tot_f / (tot_k * 1e-3) / 1e12, 1)
+    out["unit"] = "TFLOP/s"
+    out["frac"] = round(tot_f / (tot_k * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    out["torch_layer_ms"] = round(tot_t, 5)
+    # the fp64 oracle on the host, q_proj
+    inp = synthetic.row_sparse_inputs(n_rows, 2048, 2048, frac, seed)
+    xs, ws_, dys = (inp[k].to(torch.float64).numpy() for k in ("x", "w", "dy"))
+    kp = inp["keep"].numpy().astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.row_sparse_linear_bwd(xs, ws_, dys, kp)
+    sec = time.perf_counter() - t0
+    f = 4 * len(kp) * 2048 * 2048
+    out["cpu_baseline"] = {"value": round(f / sec / 1e12, 4), "unit": "TFLOP/s",
+                           "cores": torch.get_num_threads(), "kind": "oracle",
+                           "sample": "q_proj (2048 -> 2048), fp64 numpy, one call"}
+    return out
+
+
 def _pct(xs):
     import numpy as np
     a = np.asarray(xs)
@@ -316,6 +409,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="also time the fused forward + cache append against the two "
                          "separate calls, outside the step")
+    ap.add_argument("--row-sparse", type=float, default=None, metavar="FRAC",
+                    help="also time the row-sparse linear backward of one 1.7B-class "
+                         "layer's projections at 2048 tokens with this kept fraction")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM "
                          "byte counters of a profiler run)")
@@ -455,6 +551,8 @@ def main():
         out["prefix_kv_grad"] = time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
             args.steps, args.warmup)
+    if args.row_sparse is not None:
+        out["row_sparse"] = time_row_sparse(pka, args.row_sparse, args.steps, args.warmup)
     if args.decode:
         out["decode"] = time_decode(pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse), cache,
                                     args.steps, args.warmup)

@@ -188,6 +188,28 @@ pka_status pka_kv_append_f16(const pka_dims* dims, const void* k, const void* v,
 pka_status pka_kv_append_bf16(const pka_dims* dims, const void* k, const void* v,
                               const pka_cache* cache, pka_stream_t stream);
 
+/* Row-sparse linear backward of the projections next to attention ("stop-gradient
+ * through context tokens", Mechanism): q/o and the MLP keep their full-row forward
+ * y = x W^T, and their backward runs only on the K token rows that some loss term
+ * reads (the other rows' upstream gradient is zero by then):
+ *   dw = dy[keep]^T x[keep]                          f32 [out][in]
+ *   dx[keep[r]] = dy[keep[r]] W;  dx[other rows] = 0  bf16 [N][in]
+ * This equals the dense backward with dy zeroed outside the kept rows. x is bf16
+ * [N][in], w bf16 [out][in], dy bf16 [N][out], all row-major; keep is a DEVICE
+ * int32 [K] array of distinct rows of x (any order; entries outside [0, N) are
+ * skipped: they add nothing and write nothing). in_features and out_features are
+ * multiples of 128. dw or dx may be NULL, and that product is skipped; 0 <= K <= N
+ * (K = 0 writes dw = 0 and dx = 0). No workspace. Row pointers 16-byte aligned. */
+typedef struct {
+  int64_t n_rows;        /* N >= 1: rows of x, dy and dx                      */
+  int64_t n_keep;        /* K: entries of keep                                */
+  int32_t in_features;   /* columns of x and w, multiple of 128               */
+  int32_t out_features;  /* rows of w, columns of dy, multiple of 128         */
+} pka_rs_dims;
+pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, const void* w,
+                                     const void* dy, const int32_t* keep, float* dw, void* dx,
+                                     pka_stream_t stream);
+
 /* Test hook: dequantise rows [row0, row0+rows) of both K and V of a Q8_0 cache of
  * `batch` windows x `n_heads_kv` heads exactly as the attention kernels read them:
  * out_f32 = f32(scale) * code (exact), out_bf16 = bf16(out_f32) (RNE, may be NULL).
@@ -223,7 +245,10 @@ typedef enum {
   PKA_KERNEL_BWD_DKDV_REDUCE = 8, /* reserved: folded into PKA_KERNEL_BWD_DQ_REDUCE */
   PKA_KERNEL_PREFIX_KV = 9,  /* prefix dk, dv within the horizon                    */
   PKA_KERNEL_PREFIX_KV_REDUCE = 10, /* sums of their row-split partials             */
-  PKA_KERNEL_COUNT = 11
+  PKA_KERNEL_RS_ZERO = 11,   /* row-sparse backward: zeros of the rows not kept   */
+  PKA_KERNEL_RS_DX = 12,     /* row-sparse backward: dX of the kept rows          */
+  PKA_KERNEL_RS_DW = 13,     /* row-sparse backward: dW                           */
+  PKA_KERNEL_COUNT = 14
 } pka_kernel_id;
 
 pka_status pka_profile_enable(int32_t on);

@@ -9,7 +9,7 @@ Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
 ``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``,
 ``kv_append_f16``, ``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``,
 ``fwd_workspace_bytes``, ``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``,
-``profile_*``. ``chunk_attention`` wraps forward and backward in an
+``row_sparse_linear_bwd``, ``profile_*``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
 constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
 chunk loop of a batch of windows: step, append, advance every window's prefix.
@@ -43,7 +43,7 @@ STATUS = {0: "PKA_OK", 1: "PKA_ERR_NULL", 2: "PKA_ERR_DIMS", 3: "PKA_ERR_UNSUPPO
           4: "PKA_ERR_CAPACITY", 5: "PKA_ERR_ALIGN", 6: "PKA_ERR_WORKSPACE", 7: "PKA_ERR_HIP"}
 KERNELS = {"fwd": 0, "fwd_combine": 1, "bwd_prep": 2, "bwd_dq": 3, "bwd_dkdv": 4,
            "bwd_dq_reduce": 5, "append": 6, "dequant": 7, "bwd_dkdv_reduce": 8,
-           "prefix_kv": 9, "prefix_kv_reduce": 10}
+           "prefix_kv": 9, "prefix_kv_reduce": 10, "rs_zero": 11, "rs_dx": 12, "rs_dw": 13}
 
 
 class Dims(ctypes.Structure):
@@ -51,6 +51,11 @@ class Dims(ctypes.Structure):
                 ("n_heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("prefix_len", ctypes.c_int64), ("chunk_len", ctypes.c_int64),
                 ("softmax_scale", ctypes.c_float), ("prefix_lens", ctypes.c_void_p)]
+
+
+class RsDims(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_int64), ("n_keep", ctypes.c_int64),
+                ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32)]
 
 
 class CacheDesc(ctypes.Structure):
@@ -78,6 +83,8 @@ _SIGS = {
     "pka_kv_append_bf16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
     "pka_kv_dequant_q8_0": (ctypes.c_int, [_P(CacheDesc), _i32, _i32, _i64, _i64, _vp, _vp,
                                            _vp]),
+    "pka_row_sparse_linear_bwd": (ctypes.c_int, [_P(RsDims), _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp]),
     "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pka_last_error": (ctypes.c_char_p, []),
     "pka_profile_enable": (ctypes.c_int, [_i32]),
@@ -379,6 +386,39 @@ def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = 
                                     _ptr(out), _ptr(outb), _stream(cache.k.device)),
            "pka_kv_dequant_q8_0")
     return out, outb
+
+
+def row_sparse_linear_bwd(x, w, dy, keep, dw=None, dx=None, want_dw=True, want_dx=True):
+    """Backward of y = x @ w.T on the kept rows only ("stop-gradient through context
+    tokens", Mechanism): dw = dy[keep]^T x[keep] (f32 [out][in]) and dx (bf16 [N][in],
+    dy[keep] @ w on the kept rows, zero elsewhere). x [N][in], w [out][in], dy [N][out]
+    bf16 on one GPU; keep: int32 tensor [K] of distinct row indices on that GPU.
+    Returns (dw, dx); a product not wanted is skipped and returned as None."""
+    if x.dim() != 2 or w.dim() != 2 or dy.dim() != 2:
+        raise ValueError("x, w, dy must be 2-D")
+    n, fin = x.shape
+    fout = w.shape[0]
+    _tensor(x, "x", (n, fin), torch.bfloat16, x.device)
+    _tensor(w, "w", (fout, fin), torch.bfloat16, x.device)
+    _tensor(dy, "dy", (n, fout), torch.bfloat16, x.device)
+    if keep.dim() != 1:
+        raise ValueError("keep must be 1-D")
+    _tensor(keep, "keep", (keep.shape[0],), torch.int32, x.device)
+    if want_dw:
+        dw = torch.empty((fout, fin), dtype=torch.float32, device=x.device) if dw is None else dw
+        _tensor(dw, "dw", (fout, fin), torch.float32, x.device)
+    else:
+        dw = None
+    if want_dx:
+        dx = torch.empty_like(x) if dx is None else dx
+        _tensor(dx, "dx", (n, fin), torch.bfloat16, x.device)
+    else:
+        dx = None
+    dims = RsDims(n, keep.shape[0], fin, fout)
+    _check(_lib.pka_row_sparse_linear_bwd(ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(dy),
+                                          _ptr(keep), _ptr(dw), _ptr(dx), _stream(x.device)),
+           "pka_row_sparse_linear_bwd")
+    return dw, dx
 
 
 class _ChunkAttention(torch.autograd.Function):

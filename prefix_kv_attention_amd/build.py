@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libpka.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["pka_api.cpp", "kv_cache.hip", "attn_fwd.hip", "attn_bwd.hip"]
+SOURCES = ["pka_api.cpp", "kv_cache.hip", "attn_fwd.hip", "attn_bwd.hip", "row_sparse.hip"]
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", f"-I{os.path.join(ROOT, 'include')}"]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
           "-packed-fp32-ops", "-fno-gpu-rdc"]

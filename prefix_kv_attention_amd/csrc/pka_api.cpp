@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "pka_internal.hpp"
+#include "row_sparse.hpp"
 
 namespace pka {
 namespace {
@@ -565,6 +566,46 @@ pka_status pka_kv_dequant_q8_0(const pka_cache* cache, int32_t batch, int32_t n_
   p.D = cache->head_dim;
   hipError_t e = launch_dequant(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "kv_dequant_q8_0 launch");
+  return PKA_OK;
+}
+
+pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, const void* w,
+                                     const void* dy, const int32_t* keep, float* dw, void* dx,
+                                     pka_stream_t stream) {
+  g_last_error[0] = 0;
+  if (!dims) return fail(PKA_ERR_NULL, "dims is NULL");
+  const int64_t N = dims->n_rows, K = dims->n_keep;
+  const int32_t fin = dims->in_features, fout = dims->out_features;
+  if (N < 1 || K < 0 || K > N)
+    return fail(PKA_ERR_DIMS, "need n_rows >= 1 and 0 <= n_keep <= n_rows (got %lld, %lld)",
+                (long long)N, (long long)K);
+  if (fin < kRsTile || fout < kRsTile || fin % kRsTile != 0 || fout % kRsTile != 0)
+    return fail(PKA_ERR_UNSUPPORTED, "in_features (%d) and out_features (%d) must be "
+                "positive multiples of %d", fin, fout, kRsTile);
+  if (N > kMaxSeq || (int64_t)(fin / kRsTile) * ((K + kRsTile - 1) / kRsTile) > kMaxSeq ||
+      (int64_t)(fin / kRsTile) * (fout / kRsTile) > kMaxSeq || (N * (fin / 8) + 255) / 256 > kMaxSeq)
+    return fail(PKA_ERR_DIMS, "row-sparse problem too large for one launch");
+  if (!dw && !dx) return PKA_OK;
+  pka_status st;
+  if ((st = check_ptrs({dy}, "dy")) != PKA_OK) return st;
+  if (dw && (st = check_ptrs({x, dw}, "x, dw")) != PKA_OK) return st;
+  if (dx && (st = check_ptrs({w, dx}, "w, dx")) != PKA_OK) return st;
+  if (K > 0 && !keep) return fail(PKA_ERR_NULL, "keep is NULL");
+  if ((reinterpret_cast<uintptr_t>(keep) & 3u) != 0)
+    return fail(PKA_ERR_ALIGN, "keep not 4-byte aligned");
+  RsParams p{};
+  p.x = static_cast<const uint16_t*>(x);
+  p.w = static_cast<const uint16_t*>(w);
+  p.dy = static_cast<const uint16_t*>(dy);
+  p.keep = keep;
+  p.dw = dw;
+  p.dx = static_cast<uint16_t*>(dx);
+  p.N = N;
+  p.K = K;
+  p.in = fin;
+  p.out = fout;
+  hipError_t e = launch_row_sparse_bwd(p, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "row_sparse_linear_bwd launch");
   return PKA_OK;
 }
 

@@ -139,3 +139,69 @@ def small(name="small", *, batch=1, n_heads_q=2, n_heads_kv=1, head_dim=64,
     return Workload(name, batch, n_heads_q, n_heads_kv, head_dim, prefix_len,
                     chunk_len, cache_type, seed, qkv_std, prefix_std, do_std,
                     outlier_frac, head_scale)
+
+
+# ---------------------------------------------------------------------------------
+# Row-sparse linear backward ("stop-gradient through context tokens", Mechanism and
+# its single-GPU microbenchmark: a 1.7B dense model at sequence length 2048, kept
+# fractions 0.62, 0.5, 0.2, 0.1). No weights or data of that model are available;
+# these seeded tensors have the shapes of one decoder layer's projections.
+
+@dataclasses.dataclass(frozen=True)
+class RowSparseShape:
+    name: str
+    in_features: int
+    out_features: int
+
+
+# One decoder layer of a 1.7B-class dense model (hidden 2048, 16 query heads x 128,
+# MLP 6144): the projections whose backward the page makes row-sparse.
+LAYER_1_7B = (
+    RowSparseShape("q_proj", 2048, 2048),
+    RowSparseShape("o_proj", 2048, 2048),
+    RowSparseShape("gate_proj", 2048, 6144),
+    RowSparseShape("up_proj", 2048, 6144),
+    RowSparseShape("down_proj", 6144, 2048),
+)
+
+
+def kept_rows(n_rows: int, keep_frac: float, seed: int, mean_span: int = 96) -> np.ndarray:
+    """Sorted int32 indices of round(keep_frac * n_rows) kept rows, laid out as reply
+    spans between context gaps (the rows a loss reads come in runs): about
+    K / mean_span spans whose lengths, and the gaps around them, are random
+    compositions of K and N - K."""
+    rng = np.random.default_rng(seed)
+    k = int(round(keep_frac * n_rows))
+    if k == 0:
+        return np.zeros(0, dtype=np.int32)
+    s = max(1, min(k, n_rows - k + 1, k // mean_span))
+
+    def composition(total, parts, min_part):
+        cuts = np.sort(rng.choice(np.arange(1, total - parts * (min_part - 1)), parts - 1,
+                                  replace=False)) if parts > 1 else np.zeros(0, dtype=np.int64)
+        edges = np.concatenate([[0], cuts, [total - parts * (min_part - 1)]])
+        return np.diff(edges) + (min_part - 1)
+
+    spans = composition(k, s, 1)
+    gaps = composition(n_rows - k + 2, s + 1, 1) - np.array([1] + [0] * (s - 1) + [1])
+    rows, pos = [], 0
+    for i in range(s):
+        pos += int(gaps[i])
+        rows.append(np.arange(pos, pos + int(spans[i])))
+        pos += int(spans[i])
+    out = np.concatenate(rows).astype(np.int32)
+    assert len(out) == k and out[-1] < n_rows
+    return out
+
+
+def row_sparse_inputs(n_rows: int, in_features: int, out_features: int, keep_frac: float,
+                      seed: int) -> dict:
+    """x bf16 [N][in] ~ N(0, 1), w bf16 [out][in] ~ N(0, 0.02^2), dy bf16 [N][out]
+    ~ N(0, 0.01^2) (drawn in that order, torch CPU tensors) and keep int32 [K]."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_rows, in_features), dtype=np.float32)
+    w = rng.standard_normal((out_features, in_features), dtype=np.float32) * np.float32(0.02)
+    dy = rng.standard_normal((n_rows, out_features), dtype=np.float32) * np.float32(0.01)
+    keep = kept_rows(n_rows, keep_frac, seed + 1)
+    return {"x": to_bf16(x), "w": to_bf16(w), "dy": to_bf16(dy),
+            "keep": torch.from_numpy(keep)}

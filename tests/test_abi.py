@@ -269,3 +269,48 @@ def test_fwd_append_validation(pka):
     assert st == 4 and "capacity" in msg
     assert call(cache(pka, capacity=600, type=pka.CACHE_Q8_0))[0] == 1   # no scales
     assert call(cache(pka, capacity=600, k=MIS))[0] == 5
+
+
+def test_row_sparse_validation(pka):
+    """Row-sparse backward: refused on the host before any launch."""
+    lib = pka.lib
+
+    def call(n=256, k=128, fin=256, fout=384, x=A, w=A, dy=A, keep=A, dw=A, dx=A, d=True):
+        dd = pka.RsDims(n, k, fin, fout)
+        st = lib.pka_row_sparse_linear_bwd(ctypes.byref(dd) if d else None, x, w, dy, keep,
+                                           dw, dx, None)
+        return st, lib.pka_last_error().decode()
+
+    assert call(d=False)[0] == 1
+    assert call(n=0, k=0)[0] == 2
+    assert call(k=-1)[0] == 2
+    assert call(k=257)[0] == 2                        # more kept rows than rows
+    st, msg = call(fin=200)
+    assert st == 3 and "multiples of 128" in msg
+    assert call(fout=64)[0] == 3
+    assert call(dy=None)[0] == 1
+    assert call(x=None)[0] == 1                       # dw needs x
+    assert call(w=None, dx=A, dw=None)[0] == 1        # dx needs w
+    assert call(keep=None)[0] == 1
+    assert call(keep=A + 2)[0] == 5
+    assert call(dx=MIS)[0] == 5
+    assert call(dw=MIS)[0] == 5
+    assert call(dw=None, dx=None)[0] == 0             # nothing asked: nothing launched
+
+
+def test_rs_dims_layout_matches_the_header(pka, tmp_path):
+    src = tmp_path / "rs_layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "pka.h"\n'
+        "int main(void) {\n"
+        '  printf("%zu %zu %zu %zu\\n", sizeof(pka_rs_dims), offsetof(pka_rs_dims, n_keep),'
+        " offsetof(pka_rs_dims, in_features), offsetof(pka_rs_dims, out_features));\n"
+        "  return 0;\n}\n")
+    exe = tmp_path / "rs_layout"
+    subprocess.run(["gcc", "-std=c99", f"-I{os.path.dirname(HEADER)}", str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    R = pka.RsDims
+    assert got == [ctypes.sizeof(R), R.n_keep.offset, R.in_features.offset,
+                   R.out_features.offset]
