@@ -7,11 +7,11 @@
 // that stage the operand tiles in LDS, so no compacted copy of x or dY is made.
 //
 // Design (MI355X):
-//  * One kernel template for both products. A workgroup of 4 waves owns a 128 x 128
-//    output tile (each wave 64 x 64 = 2 x 2 MFMA blocks) and walks the contraction
-//    in k-stages of 64 through two LDS buffers (one barrier per stage); the rows of
-//    the stage three ahead are loaded into registers while a stage is computed. Two
-//    workgroups per CU.
+//  * One kernel template for both products. A workgroup owns a 128 x 128 output tile
+//    and walks the contraction in k-stages of 64 through two LDS buffers (one barrier
+//    per stage); the rows of the stage three ahead are loaded into registers while a
+//    stage is computed. 4 waves of 64 x 64 (2 x 2 MFMA blocks, up to two workgroups
+//    per CU), or 8 waves of 64 x 32 when the grid has at most one tile per CU.
 //  * dX is computed transposed, dX^T = W^T dY[keep]^T: its A operand is W^T, read
 //    from the row-major W tile with the transposing LDS read; its B operand is a
 //    gathered dY row, read as is. The transposing read returns each 16-deep k-step
@@ -38,10 +38,8 @@ namespace {
 
 constexpr int BT = kRsTile;     // output tile (both dimensions)
 constexpr int BK = kRsStage;    // k-stage
-constexpr int RNT = 256;        // 4 waves, 2 x 2 of 64 x 64
 constexpr int SW = BT + 8;      // row stride (elements) of the [k][128] tiles
 constexpr int SR = BK + 8;      // row stride of the dX kernel's [row][64] dY tile
-constexpr int CPT = 4;          // 16-byte chunks per thread per tile per stage
 
 enum : int { kDX = 0, kDW = 1 };
 
@@ -51,13 +49,22 @@ struct RsLds {
   uint16_t b[2][MODE == kDX ? BT * SR : BK * SW];  // dX: [row][k] dY; dW: [k][j] x rows
 };
 
-template <int MODE>
-__global__ __launch_bounds__(RNT) void row_sparse_kernel(RsParams p) {
+// Waves of a workgroup: 2 along i (64 rows each) x BT / (32 JB) along j (JB blocks of
+// 32 columns each): JB = 2 gives 4 waves of 64 x 64, JB = 1 gives 8 waves of 64 x 32
+// (two per SIMD on the same tile, for grids too small to put two workgroups on a CU).
+template <int JB>
+constexpr int rs_threads() { return 64 * 2 * (BT / (32 * JB)); }
+
+template <int MODE, int JB>
+__global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p) {
+  constexpr int RNT = rs_threads<JB>();
+  constexpr int CPT = BK * BT / 8 / RNT;   // 16-byte chunks per thread per tile per stage
   __shared__ __align__(16) RsLds<MODE> sm;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int wi = wave & 1, wj = wave >> 1;
+  const int jw = wj * 32 * JB;   // this wave's first column of the tile
 
   // dX^T: i = input feature, j = kept row (position in keep), k = output feature.
   // dW:   i = output feature, j = input feature, k = kept row.
@@ -150,12 +157,12 @@ __global__ __launch_bounds__(RNT) void row_sparse_kernel(RsParams p) {
   using S1 = std::integral_constant<int, 1>;
 
   const TrOffsets t_off = tr_lane_offsets<SW>(lane);
-  const int b_off = (wj * 64 + prow(l32)) * SR + hf * 8;   // dX: B operand rows
-  f32x16 acc[2][2];
+  const int b_off = (jw + prow(l32)) * SR + hf * 8;   // dX: B operand rows
+  f32x16 acc[2][JB];
 #pragma unroll
   for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = f32x16{};
+    for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = f32x16{};
 
   // Prologue: stage 0 into LDS, stages 1 and 2 in registers (sets 1 and 0). Loads
   // past the last stage re-read the last stage (never computed): every step then
@@ -183,23 +190,25 @@ __global__ __launch_bounds__(RNT) void row_sparse_kernel(RsParams p) {
     const int cur = st & 1;
     const uint16_t* at = sm.a[cur];
     const uint16_t* bt = sm.b[cur];
-    bf16x8 av[2][4], bv[2][4];
+    bf16x8 av[2][4], bv[JB][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        av[x][ks] = lds_tr_operand<SW>(at, t_off, ks * 16, wi * 64 + x * 32);
+      for (int x = 0; x < 2; ++x) av[x][ks] = lds_tr_operand<SW>(at, t_off, ks * 16, wi * 64 + x * 32);
+#pragma unroll
+      for (int x = 0; x < JB; ++x) {
         if constexpr (MODE == kDX)
           bv[x][ks] = *reinterpret_cast<const bf16x8*>(&bt[b_off + x * 32 * SR + ks * 16]);
         else
-          bv[x][ks] = lds_tr_operand<SW>(bt, t_off, ks * 16, wj * 64 + x * 32);
+          bv[x][ks] = lds_tr_operand<SW>(bt, t_off, ks * 16, jw + x * 32);
       }
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(av[ib][ks], bv[jb][ks], acc[ib][jb]);
+        for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = mfma32(av[ib][ks], bv[jb][ks], acc[ib][jb]);
     // The other buffer was last read in step st - 1, which every wave has left (the
     // barrier below it); after the last stage this writes rows nobody reads.
     store(set_next, cur ^ 1);
@@ -215,11 +224,11 @@ __global__ __launch_bounds__(RNT) void row_sparse_kernel(RsParams p) {
   if (st < n_st) step(S1{}, st);
 
   // Register r of block (ib, jb) is row i0 + wi*64 + ib*32 + (r/4)*8 + hf*4 + r%4 of
-  // the tile's i range, lane l32 column j0 + wj*64 + jb*32 + l32 of its j range.
+  // the tile's i range, lane l32 column j0 + jw + jb*32 + l32 of its j range.
   if constexpr (MODE == kDX) {
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      const int64_t m = j0 + wj * 64 + jb * 32 + l32;
+    for (int jb = 0; jb < JB; ++jb) {
+      const int64_t m = j0 + jw + jb * 32 + l32;
       if (m >= p.K) continue;
       const int32_t r = p.keep[m];
       if (r < 0 || r >= p.N) continue;
@@ -238,8 +247,8 @@ __global__ __launch_bounds__(RNT) void row_sparse_kernel(RsParams p) {
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb) {
-        float* dst = p.dw + (int64_t)(i0 + wi * 64 + ib * 32 + hf * 4) * p.in + j0 + wj * 64 +
+      for (int jb = 0; jb < JB; ++jb) {
+        float* dst = p.dw + (int64_t)(i0 + wi * 64 + ib * 32 + hf * 4) * p.in + j0 + jw +
                      jb * 32 + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dst[(int64_t)((r / 4) * 8 + r % 4) * p.in] = acc[ib][jb][r];
@@ -256,6 +265,21 @@ __global__ __launch_bounds__(256) void row_sparse_zero_kernel(RsParams p) {
   reinterpret_cast<u32x4*>(p.dx)[idx] = u32x4{0u, 0u, 0u, 0u};
 }
 
+template <int MODE>
+hipError_t launch_product(const RsParams& p, int64_t tiles, hipStream_t s) {
+  // Grids of at most one tile per CU run 8 waves per tile (two per SIMD); larger ones
+  // 4 waves (up to two workgroups per CU). Measured at 2048 tokens: q_proj dX 26.6 ->
+  // 25.0 us and dW 21.8 -> 20.1 us with 8 waves; down_proj dX (384 tiles) 47.6 us with
+  // 4 waves against 53.1 us with 8.
+  if (tiles <= kNumCUs)
+    hipLaunchKernelGGL((row_sparse_kernel<MODE, 1>), dim3((unsigned)tiles),
+                       dim3(rs_threads<1>()), 0, s, p);
+  else
+    hipLaunchKernelGGL((row_sparse_kernel<MODE, 2>), dim3((unsigned)tiles),
+                       dim3(rs_threads<2>()), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_row_sparse_bwd(const RsParams& p, hipStream_t s) {
@@ -268,19 +292,16 @@ hipError_t launch_row_sparse_bwd(const RsParams& p, hipStream_t s) {
     prof_end(PKA_KERNEL_RS_ZERO, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.K > 0) {
-      const int64_t tiles = (int64_t)(p.in / BT) * ((p.K + BT - 1) / BT);
       prof_begin(PKA_KERNEL_RS_DX, s);
-      hipLaunchKernelGGL(row_sparse_kernel<kDX>, dim3((unsigned)tiles), dim3(RNT), 0, s, p);
+      e = launch_product<kDX>(p, (int64_t)(p.in / BT) * ((p.K + BT - 1) / BT), s);
       prof_end(PKA_KERNEL_RS_DX, s);
-      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (e != hipSuccess) return e;
     }
   }
   if (p.dw != nullptr) {
-    const int64_t tiles = (int64_t)(p.out / BT) * (p.in / BT);
     prof_begin(PKA_KERNEL_RS_DW, s);
-    hipLaunchKernelGGL(row_sparse_kernel<kDW>, dim3((unsigned)tiles), dim3(RNT), 0, s, p);
+    e = launch_product<kDW>(p, (int64_t)(p.out / BT) * (p.in / BT), s);
     prof_end(PKA_KERNEL_RS_DW, s);
-    e = hipGetLastError();
   }
   return e;
 }
