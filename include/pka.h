@@ -199,16 +199,20 @@ pka_status pka_kv_append_bf16(const pka_dims* dims, const void* k, const void* v
  * int32 [K] array of distinct rows of x (any order; entries outside [0, N) are
  * skipped: they add nothing and write nothing). in_features and out_features are
  * multiples of 128. dw or dx may be NULL, and that product is skipped; 0 <= K <= N
- * (K = 0 writes dw = 0 and dx = 0). No workspace. Row pointers 16-byte aligned. */
+ * (K = 0 writes dw = 0 and dx = 0). Row pointers 16-byte aligned.
+ * ws: pka_row_sparse_linear_bwd_workspace_bytes(dims) bytes of device memory (may be
+ * NULL if 0; not used when dx is NULL): when few kept rows make few output tiles, the
+ * dX product is split over the output features and its fp32 partials go there. */
 typedef struct {
   int64_t n_rows;        /* N >= 1: rows of x, dy and dx                      */
   int64_t n_keep;        /* K: entries of keep                                */
   int32_t in_features;   /* columns of x and w, multiple of 128               */
   int32_t out_features;  /* rows of w, columns of dy, multiple of 128         */
 } pka_rs_dims;
+size_t pka_row_sparse_linear_bwd_workspace_bytes(const pka_rs_dims* dims);
 pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, const void* w,
                                      const void* dy, const int32_t* keep, float* dw, void* dx,
-                                     pka_stream_t stream);
+                                     void* ws, size_t ws_bytes, pka_stream_t stream);
 
 /* Test hook: dequantise rows [row0, row0+rows) of both K and V of a Q8_0 cache of
  * `batch` windows x `n_heads_kv` heads exactly as the attention kernels read them:
@@ -248,7 +252,8 @@ typedef enum {
   PKA_KERNEL_RS_ZERO = 11,   /* row-sparse backward: zeros of the rows not kept   */
   PKA_KERNEL_RS_DX = 12,     /* row-sparse backward: dX of the kept rows          */
   PKA_KERNEL_RS_DW = 13,     /* row-sparse backward: dW                           */
-  PKA_KERNEL_COUNT = 14
+  PKA_KERNEL_RS_DX_REDUCE = 14, /* row-sparse backward: sums of dX split partials */
+  PKA_KERNEL_COUNT = 15
 } pka_kernel_id;
 
 pka_status pka_profile_enable(int32_t on);

@@ -9,7 +9,7 @@ Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
 ``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``,
 ``kv_append_f16``, ``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``,
 ``fwd_workspace_bytes``, ``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``,
-``row_sparse_linear_bwd``, ``profile_*``. ``chunk_attention`` wraps forward and backward in an
+``row_sparse_linear_bwd``, ``row_sparse_workspace_bytes``, ``profile_*``. ``chunk_attention`` wraps forward and backward in an
 autograd function whose cache inputs get no gradient (they are stop-gradient
 constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
 chunk loop of a batch of windows: step, append, advance every window's prefix.
@@ -43,7 +43,8 @@ STATUS = {0: "PKA_OK", 1: "PKA_ERR_NULL", 2: "PKA_ERR_DIMS", 3: "PKA_ERR_UNSUPPO
           4: "PKA_ERR_CAPACITY", 5: "PKA_ERR_ALIGN", 6: "PKA_ERR_WORKSPACE", 7: "PKA_ERR_HIP"}
 KERNELS = {"fwd": 0, "fwd_combine": 1, "bwd_prep": 2, "bwd_dq": 3, "bwd_dkdv": 4,
            "bwd_dq_reduce": 5, "append": 6, "dequant": 7, "bwd_dkdv_reduce": 8,
-           "prefix_kv": 9, "prefix_kv_reduce": 10, "rs_zero": 11, "rs_dx": 12, "rs_dw": 13}
+           "prefix_kv": 9, "prefix_kv_reduce": 10, "rs_zero": 11, "rs_dx": 12, "rs_dw": 13,
+           "rs_dx_reduce": 14}
 
 
 class Dims(ctypes.Structure):
@@ -83,8 +84,9 @@ _SIGS = {
     "pka_kv_append_bf16": (ctypes.c_int, [_P(Dims), _vp, _vp, _P(CacheDesc), _vp]),
     "pka_kv_dequant_q8_0": (ctypes.c_int, [_P(CacheDesc), _i32, _i32, _i64, _i64, _vp, _vp,
                                            _vp]),
+    "pka_row_sparse_linear_bwd_workspace_bytes": (_sz, [_P(RsDims)]),
     "pka_row_sparse_linear_bwd": (ctypes.c_int, [_P(RsDims), _vp, _vp, _vp, _vp, _vp, _vp,
-                                                 _vp]),
+                                                 _vp, _sz, _vp]),
     "pka_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pka_last_error": (ctypes.c_char_p, []),
     "pka_profile_enable": (ctypes.c_int, [_i32]),
@@ -388,11 +390,19 @@ def kv_dequant_q8_0(cache: PrefixCache, row0: int, rows: int, want_bf16: bool = 
     return out, outb
 
 
-def row_sparse_linear_bwd(x, w, dy, keep, dw=None, dx=None, want_dw=True, want_dx=True):
+def row_sparse_workspace_bytes(n_rows: int, n_keep: int, in_features: int,
+                               out_features: int) -> int:
+    return int(_lib.pka_row_sparse_linear_bwd_workspace_bytes(
+        ctypes.byref(RsDims(n_rows, n_keep, in_features, out_features))))
+
+
+def row_sparse_linear_bwd(x, w, dy, keep, dw=None, dx=None, ws=None, want_dw=True,
+                          want_dx=True):
     """Backward of y = x @ w.T on the kept rows only ("stop-gradient through context
     tokens", Mechanism): dw = dy[keep]^T x[keep] (f32 [out][in]) and dx (bf16 [N][in],
     dy[keep] @ w on the kept rows, zero elsewhere). x [N][in], w [out][in], dy [N][out]
-    bf16 on one GPU; keep: int32 tensor [K] of distinct row indices on that GPU.
+    bf16 on one GPU; keep: int32 tensor [K] of distinct row indices on that GPU; ws: a
+    uint8 workspace of row_sparse_workspace_bytes(...) bytes (allocated if None).
     Returns (dw, dx); a product not wanted is skipped and returned as None."""
     if x.dim() != 2 or w.dim() != 2 or dy.dim() != 2:
         raise ValueError("x, w, dy must be 2-D")
@@ -415,8 +425,13 @@ def row_sparse_linear_bwd(x, w, dy, keep, dw=None, dx=None, want_dw=True, want_d
     else:
         dx = None
     dims = RsDims(n, keep.shape[0], fin, fout)
+    if ws is None and dx is not None:
+        ws = _workspace(int(_lib.pka_row_sparse_linear_bwd_workspace_bytes(ctypes.byref(dims))),
+                        x.device)
+    nws = _ws_bytes(ws, x.device)
     _check(_lib.pka_row_sparse_linear_bwd(ctypes.byref(dims), _ptr(x), _ptr(w), _ptr(dy),
-                                          _ptr(keep), _ptr(dw), _ptr(dx), _stream(x.device)),
+                                          _ptr(keep), _ptr(dw), _ptr(dx), _ptr(ws), nws,
+                                          _stream(x.device)),
            "pka_row_sparse_linear_bwd")
     return dw, dx
 

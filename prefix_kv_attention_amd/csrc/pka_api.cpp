@@ -569,10 +569,7 @@ pka_status pka_kv_dequant_q8_0(const pka_cache* cache, int32_t batch, int32_t n_
   return PKA_OK;
 }
 
-pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, const void* w,
-                                     const void* dy, const int32_t* keep, float* dw, void* dx,
-                                     pka_stream_t stream) {
-  g_last_error[0] = 0;
+static pka_status check_rs_dims(const pka_rs_dims* dims) {
   if (!dims) return fail(PKA_ERR_NULL, "dims is NULL");
   const int64_t N = dims->n_rows, K = dims->n_keep;
   const int32_t fin = dims->in_features, fout = dims->out_features;
@@ -585,14 +582,39 @@ pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, con
   if (N > kMaxSeq || (int64_t)(fin / kRsTile) * ((K + kRsTile - 1) / kRsTile) > kMaxSeq ||
       (int64_t)(fin / kRsTile) * (fout / kRsTile) > kMaxSeq || (N * (fin / 8) + 255) / 256 > kMaxSeq)
     return fail(PKA_ERR_DIMS, "row-sparse problem too large for one launch");
-  if (!dw && !dx) return PKA_OK;
+  return PKA_OK;
+}
+
+size_t pka_row_sparse_linear_bwd_workspace_bytes(const pka_rs_dims* dims) {
+  if (check_rs_dims(dims) != PKA_OK) return 0;
+  const int split = row_sparse_dx_split(dims->n_keep, dims->in_features, dims->out_features);
+  if (split <= 1) return 0;
+  return align256((size_t)split * dims->n_keep * dims->in_features * 4);
+}
+
+pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, const void* w,
+                                     const void* dy, const int32_t* keep, float* dw, void* dx,
+                                     void* ws, size_t ws_bytes, pka_stream_t stream) {
+  g_last_error[0] = 0;
   pka_status st;
+  if ((st = check_rs_dims(dims)) != PKA_OK) return st;
+  const int64_t N = dims->n_rows, K = dims->n_keep;
+  const int32_t fin = dims->in_features, fout = dims->out_features;
+  if (!dw && !dx) return PKA_OK;
   if ((st = check_ptrs({dy}, "dy")) != PKA_OK) return st;
   if (dw && (st = check_ptrs({x, dw}, "x, dw")) != PKA_OK) return st;
   if (dx && (st = check_ptrs({w, dx}, "w, dx")) != PKA_OK) return st;
   if (K > 0 && !keep) return fail(PKA_ERR_NULL, "keep is NULL");
   if ((reinterpret_cast<uintptr_t>(keep) & 3u) != 0)
     return fail(PKA_ERR_ALIGN, "keep not 4-byte aligned");
+  const int split = dx ? row_sparse_dx_split(K, fin, fout) : 1;
+  if (split > 1) {
+    const size_t need = pka_row_sparse_linear_bwd_workspace_bytes(dims);
+    if (!ws || ws_bytes < need)
+      return fail(PKA_ERR_WORKSPACE, "row-sparse dX needs %zu workspace bytes, got %zu", need,
+                  ws ? ws_bytes : (size_t)0);
+    if (!aligned16(ws)) return fail(PKA_ERR_ALIGN, "workspace not 16-byte aligned");
+  }
   RsParams p{};
   p.x = static_cast<const uint16_t*>(x);
   p.w = static_cast<const uint16_t*>(w);
@@ -604,6 +626,8 @@ pka_status pka_row_sparse_linear_bwd(const pka_rs_dims* dims, const void* x, con
   p.K = K;
   p.in = fin;
   p.out = fout;
+  p.dx_split = split;
+  p.ws = split > 1 ? static_cast<float*>(ws) : nullptr;
   hipError_t e = launch_row_sparse_bwd(p, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "row_sparse_linear_bwd launch");
   return PKA_OK;

@@ -24,6 +24,9 @@
 //    Each kept-row index is loaded two stages before the rows it addresses.
 //  * dX is zeroed by a streaming fill launched before the dX product, which then
 //    writes the kept rows: right for distinct kept rows in any order.
+//  * A dX grid of fewer tiles than CUs is split over the output features: fp32
+//    partials in the caller's workspace, summed in split order by a reduction that
+//    writes the kept rows.
 //  * Workgroups are renumbered so each XCD works on a contiguous range of tiles that
 //    form a near-square block of the output: the operand rows of the block stay in
 //    that XCD's L2 (q_proj at 2048 tokens: HBM fetch of the dX product 70 MB with
@@ -70,7 +73,10 @@ __global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p
   // dW:   i = output feature, j = input feature, k = kept row.
   const int TI = (MODE == kDX ? p.in : p.out) / BT;
   const int TJ = MODE == kDX ? (int)((p.K + BT - 1) / BT) : p.in / BT;
-  const int L = xcd_logical_id(blockIdx.x, TI * TJ);
+  const int SPL = MODE == kDX ? p.dx_split : 1;   // splits of the contraction
+  const int Lg = xcd_logical_id(blockIdx.x, TI * TJ * SPL);
+  const int sp = Lg / (TI * TJ);                  // this workgroup's split
+  const int L = Lg - sp * TI * TJ;
   // Each XCD's contiguous range of ids walks groups of GM i-tiles across all j-tiles,
   // so the range covers a near-square block of the output and its L2 holds the rows
   // of both operands that the block needs (GM: the power of 2 nearest the square
@@ -83,7 +89,9 @@ __global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p
   const int in_group = L - group * GM * TJ;
   const int i0 = (first + in_group % gsz) * BT, j0 = (in_group / gsz) * BT;
   const int64_t KD = MODE == kDX ? (int64_t)p.out : p.K;   // contraction length
-  const int n_st = (int)((KD + BK - 1) / BK);
+  const int n_all = (int)((KD + BK - 1) / BK);
+  const int st0 = (int)((int64_t)sp * n_all / SPL);          // this split's k-stages
+  const int n_st = (int)((int64_t)(sp + 1) * n_all / SPL) - st0;
 
   // Staging: thread tid stages chunks c = tid + s * RNT (s < CPT) of each tile.
   // [k][128] tiles: row c / 16, 8 values at column 8 (c % 16). The dX kernel's dY
@@ -112,13 +120,13 @@ __global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p
     constexpr int R = decltype(set)::value;
 #pragma unroll
     for (int s = 0; s < CPT; ++s) {
-      const int64_t k = (int64_t)st * BK + (tid + s * RNT) / 16;
+      const int64_t k = (int64_t)(st0 + st) * BK + (tid + s * RNT) / 16;
       kidx[R][s] = p.keep[k < p.K ? k : 0];
     }
   };
   auto issue = [&](auto set, int st) {
     constexpr int R = decltype(set)::value;
-    const int64_t k0 = (int64_t)st * BK;
+    const int64_t k0 = (int64_t)(st0 + st) * BK;
 #pragma unroll
     for (int s = 0; s < CPT; ++s) {
       const int c = tid + s * RNT;
@@ -225,7 +233,22 @@ __global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p
 
   // Register r of block (ib, jb) is row i0 + wi*64 + ib*32 + (r/4)*8 + hf*4 + r%4 of
   // the tile's i range, lane l32 column j0 + jw + jb*32 + l32 of its j range.
-  if constexpr (MODE == kDX) {
+  if (MODE == kDX && SPL > 1) {
+    // fp32 partials of this split, rows in kept order: [split][K][in]
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int64_t m = j0 + jw + jb * 32 + l32;
+      if (m >= p.K) continue;
+      float* dst = p.ws + ((int64_t)sp * p.K + m) * p.in + i0 + wi * 64 + hf * 4;
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(dst + ib * 32 + g4 * 8) =
+              f32x4{acc[ib][jb][g4 * 4 + 0], acc[ib][jb][g4 * 4 + 1],
+                    acc[ib][jb][g4 * 4 + 2], acc[ib][jb][g4 * 4 + 3]};
+    }
+  } else if constexpr (MODE == kDX) {
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) {
       const int64_t m = j0 + jw + jb * 32 + l32;
@@ -265,6 +288,31 @@ __global__ __launch_bounds__(256) void row_sparse_zero_kernel(RsParams p) {
   reinterpret_cast<u32x4*>(p.dx)[idx] = u32x4{0u, 0u, 0u, 0u};
 }
 
+// dX split over output features: the partials of each kept row summed in split order
+// (deterministic), rounded to bf16 and written to its row of dX.
+__global__ __launch_bounds__(256) void row_sparse_dx_reduce_kernel(RsParams p) {
+  const int ch = p.in / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m = idx / ch;
+  if (m >= p.K) return;
+  const int32_t r = p.keep[m];
+  if (r < 0 || r >= p.N) return;
+  const int c8 = (int)(idx % ch);
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < p.dx_split; ++sp) {
+    const f32x4* v = reinterpret_cast<const f32x4*>(p.ws + ((int64_t)sp * p.K + m) * p.in + c8 * 8);
+    const f32x4 a = v[0], b = v[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] += a[i];
+      o[4 + i] += b[i];
+    }
+  }
+  *reinterpret_cast<u32x4*>(p.dx + (int64_t)r * p.in + c8 * 8) =
+      u32x4{pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3]), pack_bf16(o[4], o[5]),
+            pack_bf16(o[6], o[7])};
+}
+
 template <int MODE>
 hipError_t launch_product(const RsParams& p, int64_t tiles, hipStream_t s) {
   // Grids of at most one tile per CU run 8 waves per tile (two per SIMD); larger ones
@@ -282,6 +330,16 @@ hipError_t launch_product(const RsParams& p, int64_t tiles, hipStream_t s) {
 
 }  // namespace
 
+int row_sparse_dx_split(int64_t n_keep, int in_features, int out_features) {
+  const int64_t tiles = (int64_t)(in_features / BT) * ((n_keep + BT - 1) / BT);
+  if (tiles == 0 || tiles >= kNumCUs) return 1;
+  int64_t split = kNumCUs / tiles;
+  const int64_t by_stages = (out_features / BK) / 4;   // >= 4 k-stages per split
+  if (split > by_stages) split = by_stages;
+  if (split > 8) split = 8;
+  return split < 1 ? 1 : (int)split;
+}
+
 hipError_t launch_row_sparse_bwd(const RsParams& p, hipStream_t s) {
   hipError_t e = hipSuccess;
   if (p.dx != nullptr) {
@@ -293,9 +351,17 @@ hipError_t launch_row_sparse_bwd(const RsParams& p, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.K > 0) {
       prof_begin(PKA_KERNEL_RS_DX, s);
-      e = launch_product<kDX>(p, (int64_t)(p.in / BT) * ((p.K + BT - 1) / BT), s);
+      e = launch_product<kDX>(p, (int64_t)(p.in / BT) * ((p.K + BT - 1) / BT) * p.dx_split, s);
       prof_end(PKA_KERNEL_RS_DX, s);
       if (e != hipSuccess) return e;
+      if (p.dx_split > 1) {
+        const int64_t threads = p.K * (p.in / 8);
+        prof_begin(PKA_KERNEL_RS_DX_REDUCE, s);
+        hipLaunchKernelGGL(row_sparse_dx_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
+                           dim3(256), 0, s, p);
+        prof_end(PKA_KERNEL_RS_DX_REDUCE, s);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+      }
     }
   }
   if (p.dw != nullptr) {

@@ -275,10 +275,11 @@ def test_row_sparse_validation(pka):
     """Row-sparse backward: refused on the host before any launch."""
     lib = pka.lib
 
-    def call(n=256, k=128, fin=256, fout=384, x=A, w=A, dy=A, keep=A, dw=A, dx=A, d=True):
+    def call(n=256, k=128, fin=256, fout=384, x=A, w=A, dy=A, keep=A, dw=A, dx=A, d=True,
+             ws=A, ws_bytes=1 << 40):
         dd = pka.RsDims(n, k, fin, fout)
         st = lib.pka_row_sparse_linear_bwd(ctypes.byref(dd) if d else None, x, w, dy, keep,
-                                           dw, dx, None)
+                                           dw, dx, ws, ws_bytes, None)
         return st, lib.pka_last_error().decode()
 
     assert call(d=False)[0] == 1
@@ -296,6 +297,16 @@ def test_row_sparse_validation(pka):
     assert call(dx=MIS)[0] == 5
     assert call(dw=MIS)[0] == 5
     assert call(dw=None, dx=None)[0] == 0             # nothing asked: nothing launched
+    # few kept rows: the dX product is split over the output features into a workspace
+    need = pka.row_sparse_workspace_bytes(512, 128, 256, 2048)
+    assert need >= 2 * 128 * 256 * 4 and need % 256 == 0
+    st, msg = call(n=512, k=128, fin=256, fout=2048, ws=None)
+    assert st == 6 and "workspace" in msg
+    assert call(n=512, k=128, fin=256, fout=2048, ws=A, ws_bytes=need - 1)[0] == 6
+    assert call(n=512, k=128, fin=256, fout=2048, ws=MIS, ws_bytes=need)[0] == 5
+    # many tiles: no split, no workspace; invalid dims: 0
+    assert pka.row_sparse_workspace_bytes(4096, 4096, 4096, 4096) == 0
+    assert pka.row_sparse_workspace_bytes(512, 128, 200, 2048) == 0
 
 
 def test_rs_dims_layout_matches_the_header(pka, tmp_path):

@@ -10,9 +10,10 @@ Tolerances. The inputs are bf16 (exact in fp64) and the kernels accumulate in fp
   * dX rows that are not kept must be exactly zero.
 Cases span several 128 x 128 tiles with ragged kept-row counts (K not a multiple of
 the 64-row k-stage or of the 128-row tile), a single kept row, no kept row, every row
-kept, an unsorted kept list, entries outside [0, N), one product at a time, and the
-projection shapes of a 1.7B-class layer at sequence length 2048 (kept fraction 0.5,
-checked in full against the oracle).
+kept, few kept rows (the dX product split over output features into a workspace, 2
+and 8 splits), an unsorted kept list, entries outside [0, N), one product at a time,
+and the projection shapes of a 1.7B-class layer at sequence length 2048 (kept
+fraction 0.5, checked in full against the oracle).
 """
 import numpy as np
 import pytest
@@ -64,14 +65,20 @@ CASES = [  # (name, N, in, out, kept fraction, seed)
     ("tiles-3x5", 640, 384, 640, 0.62, 2),
     ("k1", 512, 128, 128, 1 / 512, 3),
     ("all-kept", 256, 256, 128, 1.0, 4),
-    ("frac0.1", 2048, 256, 512, 0.1, 5),
+    ("frac0.1-dx-split2", 2048, 256, 512, 0.1, 5),
+    ("dx-split8-ragged", 700, 256, 2048, 0.19, 12),
 ]
 
 
 @pytest.mark.parametrize("name,n,fin,fout,frac,seed", CASES, ids=[c[0] for c in CASES])
 def test_row_sparse_matches_oracle(name, n, fin, fout, frac, seed):
-    print(f"{name} N{n} in{fin} out{fout} frac{frac}", flush=True)
+    import prefix_kv_attention_amd as pka
     inp = synthetic.row_sparse_inputs(n, fin, fout, frac, seed)
+    k = inp["keep"].numel()
+    print(f"{name} N{n} in{fin} out{fout} K{k} ws {pka.row_sparse_workspace_bytes(n, k, fin, fout)}",
+          flush=True)
+    if "split" in name:
+        assert pka.row_sparse_workspace_bytes(n, k, fin, fout) > 0
     dw, dx = run(inp)
     check(inp, dw, dx)
 
