@@ -200,8 +200,8 @@ def time_row_sparse(pka, frac, steps, warmup, n_rows=2048, seed=11):
     through context tokens", Mechanism and its microbenchmark: a 1.7B dense model at
     sequence length 2048): q, o (2048 -> 2048), gate, up (2048 -> 6144) and down
     (6144 -> 2048), with round(frac * 2048) kept rows in reply spans. Kernel times
-    from HIP events around each launch; work 2 * K * in * out FLOP for dW and the same
-    for dX. Also timed, as context: the same two products with torch on the GPU
+    from HIP events around each launch (zero fill, dX product, its split reduction when
+    split, dW product); work 2 * K * in * out FLOP for dW and the same for dX. Also timed, as context: the same two products with torch on the GPU
     (index_select of the kept rows, two hipBLASLt matmuls, zero and index_copy of
     dX), and the fp64 oracle on the host for q_proj."""
     import numpy as np
@@ -228,13 +228,14 @@ def time_row_sparse(pka, frac, steps, warmup, n_rows=2048, seed=11):
             run()
         torch.cuda.synchronize()
         pka.profile_reset()
-        pka.profile_select(["rs_zero", "rs_dx", "rs_dw"])
+        pka.profile_select(["rs_zero", "rs_dx", "rs_dx_reduce", "rs_dw"])
         pka.profile_enable(True)
         for _ in range(steps):
             run()
         torch.cuda.synchronize()
         pka.profile_enable(False)
-        t = {k: pka.profile_read(k)[0] / steps for k in ("rs_zero", "rs_dx", "rs_dw")}
+        t = {k: pka.profile_read(k)[0] / steps
+             for k in ("rs_zero", "rs_dx", "rs_dx_reduce", "rs_dw")}
         kl = keep.long()
 
         def ref():
@@ -253,14 +254,16 @@ def time_row_sparse(pka, frac, steps, warmup, n_rows=2048, seed=11):
         torch.cuda.synchronize()
         t_ref = ev[0].elapsed_time(ev[1]) / steps
         f = 2 * K * proj.in_features * proj.out_features
-        k_ms = t["rs_zero"] + t["rs_dx"] + t["rs_dw"]
+        k_ms = t["rs_zero"] + t["rs_dx"] + t["rs_dx_reduce"] + t["rs_dw"]
         tot_k += k_ms
         tot_t += t_ref
         tot_f += 2 * f
         out["projections"][proj.name] = {
             "in": proj.in_features, "out": proj.out_features, "n_keep": K,
             "zero_ms": round(t["rs_zero"], 5), "dx_ms": round(t["rs_dx"], 5),
-            "dw_ms": round(t["rs_dw"], 5),
+            "dx_reduce_ms": round(t["rs_dx_reduce"], 5), "dw_ms": round(t["rs_dw"], 5),
+            "ws_bytes": pka.row_sparse_workspace_bytes(n_rows, K, proj.in_features,
+                                                      proj.out_features),
             "dx_tflops": round(f / (t["rs_dx"] * 1e-3) / 1e12, 1),
             "dw_tflops": round(f / (t["rs_dw"] * 1e-3) / 1e12, 1),
             "torch_ms": round(t_ref, 5)}
