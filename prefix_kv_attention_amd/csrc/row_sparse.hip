@@ -79,8 +79,8 @@ __global__ __launch_bounds__(rs_threads<JB>()) void row_sparse_kernel(RsParams p
   const int L = Lg - sp * TI * TJ;
   // Each XCD's contiguous range of ids walks groups of GM i-tiles across all j-tiles,
   // so the range covers a near-square block of the output and its L2 holds the rows
-  // of both operands that the block needs (GM: the power of 2 nearest the square
-  // root of the range, at most TI).
+  // of both operands that the block needs (GM: the largest power of 2 whose square
+  // fits in one XCD's share of the tiles, at most TI).
   const int per_xcd = (TI * TJ + kNumXCDs - 1) / kNumXCDs;
   int GM = 1;
   while (GM * 2 <= TI && GM * GM * 4 <= per_xcd) GM *= 2;
