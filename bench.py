@@ -13,9 +13,12 @@ not). `roofline` is for the dominant kernel (bwd_dq), timed live with HIP events
 around each of its launches inside the timed region. `cpu_baseline` times the
 fp64 oracle on a bounded sample of the same workload.
 
---row-sparse FRAC adds the row-sparse linear backward of the projections next to
-attention ("stop-gradient through context tokens", Mechanism) for one 1.7B-class
-layer at 2048 tokens, outside the step (object `row_sparse`).
+After the step, and outside its timing, the calls of the rows beyond the step are
+timed on their own (skip them all with --no-next): the prefix gradient within a
+horizon (`prefix_kv_grad`, H = 4096), the fused forward + cache append against the two
+separate calls (`decode`), and the row-sparse linear backward of the projections next
+to attention ("stop-gradient through context tokens", Mechanism) for one 1.7B-class
+layer at 2048 tokens with half the rows kept (`row_sparse`).
 
 Warm-up: the --warmup steps, then more untimed steps until --warmup-ms (250) has
 passed. From idle, the GPU's clocks take some tens of ms of load to settle (a
@@ -401,20 +404,22 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the step without the per-kernel HIP events")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--prefix-horizon", type=int, default=0,
+    ap.add_argument("--prefix-horizon", type=int, default=4096,
                     help="also time pka_prefix_kv_grad (dK/dV of the last H prefix rows) "
-                         "on the same inputs, outside the step")
+                         "on the same inputs, outside the step (0: skip)")
     ap.add_argument("--no-phases", action="store_true",
                     help="skip the untimed warm / cold passes that time fwd_append and bwd "
                          "separately")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph")
-    ap.add_argument("--decode", action="store_true",
-                    help="also time the fused forward + cache append against the two "
-                         "separate calls, outside the step")
-    ap.add_argument("--row-sparse", type=float, default=None, metavar="FRAC",
-                    help="also time the row-sparse linear backward of one 1.7B-class "
-                         "layer's projections at 2048 tokens with this kept fraction")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip timing the fused forward + cache append against the two "
+                         "separate calls (outside the step)")
+    ap.add_argument("--row-sparse", type=float, default=0.5, metavar="FRAC",
+                    help="kept fraction for timing the row-sparse linear backward of one "
+                         "1.7B-class layer's projections at 2048 tokens (< 0: skip)")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the prefix-gradient, decode and row-sparse legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (scales the HBM "
                          "byte counters of a profiler run)")
@@ -550,15 +555,24 @@ def main():
         g_ms = time_graph(step, args.steps, args.warmup)
         out["graph"] = {"ms_per_step": g_ms, "value": round((fwd_f + bwd_f) / (g_ms * 1e-3)
                                                             / 1e12, 2)}
-    if args.prefix_horizon > 0:
-        out["prefix_kv_grad"] = time_prefix_kv_grad(
+    # The calls of the NEXT rows, each outside the step and after it. A failure is
+    # reported in its own object and does not lose the step's line.
+    def leg(name, fn):
+        try:
+            out[name] = fn()
+        except Exception as e:  # noqa: BLE001
+            out[name] = {"error": f"{type(e).__name__}: {e}"}
+
+    if not args.no_next and args.prefix_horizon > 0:
+        leg("prefix_kv_grad", lambda: time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,
-            args.steps, args.warmup)
-    if args.row_sparse is not None:
-        out["row_sparse"] = time_row_sparse(pka, args.row_sparse, args.steps, args.warmup)
-    if args.decode:
-        out["decode"] = time_decode(pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse), cache,
-                                    args.steps, args.warmup)
+            args.steps, args.warmup))
+    if not args.no_next and not args.no_decode:
+        leg("decode", lambda: time_decode(pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse),
+                                          cache, args.steps, args.warmup))
+    if not args.no_next and args.row_sparse >= 0:
+        leg("row_sparse", lambda: time_row_sparse(pka, args.row_sparse, args.steps,
+                                                  args.warmup))
     if not args.no_cpu_baseline:
         # The step is deterministic: one more recomputes the outputs the oracle checks.
         fwd_append()
