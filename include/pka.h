@@ -199,10 +199,14 @@ pka_status pka_kv_append_bf16(const pka_dims* dims, const void* k, const void* v
  * int32 [K] array of distinct rows of x (any order; entries outside [0, N) are
  * skipped: they add nothing and write nothing). in_features and out_features are
  * multiples of 128. dw or dx may be NULL, and that product is skipped; 0 <= K <= N
- * (K = 0 writes dw = 0 and dx = 0). Row pointers 16-byte aligned.
- * ws: pka_row_sparse_linear_bwd_workspace_bytes(dims) bytes of device memory (may be
- * NULL if 0; not used when dx is NULL): when few kept rows make few output tiles, the
- * dX product is split over the output features and its fp32 partials go there. */
+ * (K = 0 writes dw = 0 and dx = 0). x, w, dy, dw, dx and ws 16-byte aligned, keep
+ * 4-byte aligned; all are caller-owned device memory.
+ * ws: pka_row_sparse_linear_bwd_workspace_bytes(dims) bytes (may be NULL if 0; not used
+ * when dx is NULL): when few kept rows make few output tiles, the dX product is split
+ * over the output features and its fp32 partials go there. Results are deterministic.
+ * Errors (nothing launched): PKA_ERR_DIMS (N < 1, K outside [0, N], a grid too large),
+ * PKA_ERR_UNSUPPORTED (features not multiples of 128), PKA_ERR_NULL / PKA_ERR_ALIGN
+ * (a needed pointer), PKA_ERR_WORKSPACE (ws missing or too small). */
 typedef struct {
   int64_t n_rows;        /* N >= 1: rows of x, dy and dx                      */
   int64_t n_keep;        /* K: entries of keep                                */
