@@ -11,7 +11,8 @@ Tolerances. The inputs are bf16 (exact in fp64) and the kernels accumulate in fp
 Cases span several 128 x 128 tiles with ragged kept-row counts (K not a multiple of
 the 64-row k-stage or of the 128-row tile), a single kept row, no kept row, every row
 kept, few kept rows (the dX product split over output features into a workspace, 2
-and 8 splits), an unsorted kept list, entries outside [0, N), one product at a time,
+and 8 splits), grids of over 500 tiles (both products, ragged K), an unsorted kept
+list, entries outside [0, N), one product at a time,
 and the projection shapes of a 1.7B-class layer at sequence length 2048 (kept
 fraction 0.5, checked in full against the oracle).
 """
@@ -67,6 +68,8 @@ CASES = [  # (name, N, in, out, kept fraction, seed)
     ("all-kept", 256, 256, 128, 1.0, 4),
     ("frac0.1-dx-split2", 2048, 256, 512, 0.1, 5),
     ("dx-split8-ragged", 700, 256, 2048, 0.19, 12),
+    ("big-dw-grid-k350", 700, 2048, 4096, 0.5, 13),        # 512 dW tiles, ragged K
+    ("big-dx-grid-k2058", 2100, 4096, 256, 0.98, 14),      # 544 dX tiles, ragged K
 ]
 
 
