@@ -1,7 +1,8 @@
 """A chunk step captured in a HIP graph and replayed.
 
 The library makes no allocation, memset or synchronisation inside its calls, so one
-step (forward, backward, append into the cache) can be captured with torch.cuda.graph
+step (forward, backward, append into the cache; the forward and the append as separate
+calls or as one fused launch) can be captured with torch.cuda.graph
 and replayed, which removes the launch overhead of small workloads. The kernels are
 deterministic: every replay must reproduce the eager step bitwise (O, LSE, dQ, dK, dV
 and the appended cache rows). Replays are separated by eager work and synchronisation,
@@ -30,10 +31,11 @@ GRAPH_CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["fwd-then-append", "fwd_append"])
 @pytest.mark.parametrize("w", GRAPH_CASES, ids=lambda w: w.name)
-def test_step_graph_replays_match_eager(w):
+def test_step_graph_replays_match_eager(w, fused):
     import prefix_kv_attention_amd as pka
-    print(f"{w.name} P{w.prefix_len} C{w.chunk_len} {w.cache_type}", flush=True)
+    print(f"{w.name} P{w.prefix_len} C{w.chunk_len} {w.cache_type} fused={fused}", flush=True)
     x = synthetic.make_inputs(w)
     d = {k: v.to(DEV) for k, v in x.items()}
     B, Hq, Hkv, D, P, C = w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, w.prefix_len, w.chunk_len
@@ -51,10 +53,15 @@ def test_step_graph_replays_match_eager(w):
             "dq": torch.empty_like(q), "dk": torch.empty_like(kc), "dv": torch.empty_like(vc)}
 
     def step():
-        pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=outs["o"], lse=outs["lse"], ws=ws_f)
+        if fused:   # the bench's step: forward and append in one launch, then backward
+            pka.chunk_attn_fwd_append(q, kc, vc, cache, P, sc, o=outs["o"], lse=outs["lse"],
+                                      ws=ws_f)
+        else:
+            pka.chunk_attn_fwd(q, kc, vc, cache, P, sc, o=outs["o"], lse=outs["lse"], ws=ws_f)
         pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, outs["o"], outs["lse"], do, dq=outs["dq"],
                            dk=outs["dk"], dv=outs["dv"], ws=ws_b)
-        pka.kv_append(kc, vc, cache, P)
+        if not fused:
+            pka.kv_append(kc, vc, cache, P)
 
     def snapshot():
         snap = {k: v.clone() for k, v in outs.items()}
