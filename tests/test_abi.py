@@ -325,3 +325,48 @@ def test_rs_dims_layout_matches_the_header(pka, tmp_path):
     R = pka.RsDims
     assert got == [ctypes.sizeof(R), R.n_keep.offset, R.in_features.offset,
                    R.out_features.offset]
+
+
+def _dkv_splits(batch, hq, hkv, C, cus=256, kb=128):
+    """The chunk dK/dV split rule, restated: one workgroup per (window, KV head, block
+    of 128 keys); while the CU budget allows, another split goes to the block whose
+    workgroups have the most 64-row steps (first on ties), each block keeping >= 2
+    steps per split and at most 16 splits. Returns the largest split count."""
+    G, groups, nkb = hq // hkv, batch * hkv, -(-C // kb)
+    if groups * nkb >= cus:
+        return 1
+    steps = [-(-(G * (C - k * kb)) // 64) for k in range(nkb)]
+    cnt = [1] * nkb
+    for _ in range(cus // groups - nkb):
+        best, load = -1, 0
+        for k in range(nkb):
+            if cnt[k] >= min(steps[k] // 2, 16):
+                continue
+            lk = -(-steps[k] // cnt[k])
+            if lk > load:
+                best, load = k, lk
+        if best < 0:
+            break
+        cnt[best] += 1
+    return max(cnt)
+
+
+@pytest.mark.parametrize("shape", [(4, 32, 8, 16384, 512), (2, 12, 2, 16384, 512),
+                                   (1, 40, 8, 63488, 512), (1, 4, 1, 1000, 130),
+                                   (8, 32, 8, 4096, 512)])
+def test_bwd_workspace_follows_the_dkv_split_rule(pka, shape):
+    B, hq, hkv, P, C = shape
+    d = dims(pka, batch=B, n_heads_q=hq, n_heads_kv=hkv, prefix_len=P, chunk_len=C)
+    a256 = lambda n: (n + 255) // 256 * 256
+    nrow = B * hq * C
+    split = _dkv_splits(B, hq, hkv, C)
+    want = a256(nrow * 4)
+    if split > 1:
+        want += a256(split * 2 * B * hkv * C * 128 * 4)
+    ws = pka.bwd_workspace_bytes(d)
+    if pka.fwd_workspace_bytes(d) == 0:          # no prefix split: delta + dK/dV partials
+        assert ws == want, (ws, want, split)
+    else:                                        # plus the dQ partials of the split
+        assert ws > want and (ws - want) % (nrow * 128 * 4) == 0
+    if shape == (4, 32, 8, 16384, 512):
+        assert split == 3                        # blocks of 32, 24, 16, 8 steps: 3, 2, 2, 1
