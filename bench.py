@@ -98,39 +98,136 @@ def read_traffic(kernel_name):
         return None
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if not readable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_group_worker(args):
+    """One (window, KV head) group through the fp64 oracle, forward then backward, in a
+    pool worker with one BLAS thread. args: (path of the group's .npz inputs, softmax
+    scale); the arrays travel through a file because the pool's pipe moves ~100 MB/s
+    and would serialise the workers' start. Returns its outputs and seconds."""
+    import numpy as np
+    import oracle
+    path, sc = args
+    with np.load(path) as z:
+        q, kc, vc, kp, vp, do = (z[k] for k in ("q", "kc", "vc", "kp", "vp", "do"))
+    t0 = time.perf_counter()
+    o, lse = oracle.group_fwd(q, kc, vc, kp, vp, sc)
+    dq, dk, dv, _ = oracle.group_bwd(q, kc, vc, kp, vp, sc, do)
+    return (o, lse, dq, dk, dv), time.perf_counter() - t0
+
+
+def _pool_init():
+    import oracle  # noqa: F401  (imported before the timed tasks)
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except Exception:  # noqa: BLE001
+        pass
+
+
+def _start(x):
+    time.sleep(0.5)   # long enough that every worker of the pool takes one
+    return x
+
+
+def cpu_workers():
+    """Workers of the oracle's process pool: the host's cores, at most 16 (a GPU machine
+    gives one GPU's job a 16-core share whatever os.cpu_count() shows)."""
+    return max(1, min(os.cpu_count() or 1, 16))
+
+
 def cpu_baseline(w, inputs, budget_s=15.0, gpu_out=None):
-    """Time the fp64 oracle on (window, KV head) groups until ~budget_s is spent. With
-    gpu_out (host copies of the step's O, LSE, dQ, dK, dV) it also reports the GPU's
-    errors against the oracle on the groups it computed."""
+    """Time the fp64 oracle (forward + backward) over the workload's (window, KV head)
+    groups with a process pool of cpu_workers() workers, one BLAS thread each, in
+    whole rounds of the pool until the groups are done or about budget_s of wall
+    time is spent (the first round sizes the rest); also the oracle's
+    conversion of the chunk's K/V rows into the cache (the append) for the workload's
+    cache type and for q8_0. With gpu_out (host copies of the step's O, LSE, dQ, dK,
+    dV) it also reports the GPU's errors against the oracle on the groups computed."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
     import numpy as np
     import oracle
     from oracle.cache import from_torch_bf16
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
     G = w.group
     sc = w.softmax_scale
-    done, spent, fl = 0, 0.0, 0.0
-    acc, lse_err = {}, 0.0
     fwd_f, bwd_f, _ = flops(w)
     per_group = (fwd_f + bwd_f) / (w.batch * w.n_heads_kv)
     groups = [(b, kv) for b in range(w.batch) for kv in range(w.n_heads_kv)]
-    for b, kv in groups:
+    f = lambda t: from_torch_bf16(t).astype(np.float64)
+    workers = cpu_workers()
+
+    import tempfile
+    tmp_root = "/dev/shm" if os.path.isdir("/dev/shm") else None
+    tmp = tempfile.TemporaryDirectory(prefix="pka_oracle_", dir=tmp_root)
+
+    def args_of(b, kv):
         hs = slice(kv * G, (kv + 1) * G)
-        f = lambda t: from_torch_bf16(t).astype(np.float64)
         kp = oracle.build_prefix(from_torch_bf16(inputs["kp"][b, kv]), w.cache_type)["values"]
         vp = oracle.build_prefix(from_torch_bf16(inputs["vp"][b, kv]), w.cache_type)["values"]
-        q, kc, vc, do = f(inputs["q"][b, hs]), f(inputs["kc"][b, kv]), f(inputs["vc"][b, kv]), \
-            f(inputs["do"][b, hs])
+        path = os.path.join(tmp.name, f"g{b}_{kv}.npz")
+        np.savez(path, q=f(inputs["q"][b, hs]), kc=f(inputs["kc"][b, kv]),
+                 vc=f(inputs["vc"][b, kv]), kp=kp, vp=vp, do=f(inputs["do"][b, hs]))
+        return path, sc
+
+    ctx = mp.get_context("spawn")   # fresh interpreters: the parent holds the GPU
+    with tmp, ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
+                                  initializer=_pool_init) as ex:
+        list(ex.map(_start, range(workers)))         # start every worker, untimed
+        # a first round of the pool sizes the sample to the budget
+        first = groups[:workers]
+        args = [args_of(b, kv) for b, kv in first]    # cache conversion, untimed
         t0 = time.perf_counter()
-        ro, rl = oracle.group_fwd(q, kc, vc, kp, vp, sc)
-        rdq, rdk, rdv, _ = oracle.group_bwd(q, kc, vc, kp, vp, sc, do)
-        spent += time.perf_counter() - t0
-        done += 1
-        fl += per_group
-        if gpu_out is not None:
+        res = list(ex.map(_oracle_group_worker, args))
+        wall = time.perf_counter() - t0
+        cpu_s = sum(r[1] for r in res)
+        done = list(zip(first, res))
+        rest = groups[workers:]
+        if rest and wall < budget_s:
+            rounds = int((budget_s - wall) / max(wall, 1e-9))
+            more = rest[:max(0, rounds) * workers]
+            if more:
+                args = [args_of(b, kv) for b, kv in more]
+                t0 = time.perf_counter()
+                res2 = list(ex.map(_oracle_group_worker, args))
+                wall += time.perf_counter() - t0
+                cpu_s += sum(r[1] for r in res2)
+                done += list(zip(more, res2))
+    n = len(done)
+    out = {"value": per_group * n / wall / 1e12, "unit": "TFLOP/s", "cores": workers,
+           "kind": "oracle",
+           "sample": f"{n} of {len(groups)} (window, KV head) groups of {w.name} "
+                     f"({G} query heads x {w.chunk_len} rows vs {w.prefix_len + w.chunk_len} "
+                     f"keys each), fp64 forward + backward, a pool of {workers} processes "
+                     f"with one BLAS thread each: {wall:.1f} s wall, {cpu_s:.1f} s summed over the workers",
+           "workers": workers, "blas_threads_per_worker": 1,
+           "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model(),
+           "wall_s": round(wall, 3), "worker_s": round(cpu_s, 3)}
+    # The append: the oracle's conversion of the chunk's K and V rows of every
+    # (window, KV head) into the cache's storage, in one process.
+    kc, vc = from_torch_bf16(inputs["kc"]), from_torch_bf16(inputs["vc"])
+    app = {}
+    for ct in dict.fromkeys((w.cache_type, "q8_0")):
+        t0 = time.perf_counter()
+        oracle.append_rows(kc, ct)
+        oracle.append_rows(vc, ct)
+        app[ct] = round((time.perf_counter() - t0) * 1e3, 3)
+    out["append_ms"] = app
+    out["append_rows"] = int(2 * kc.shape[0] * kc.shape[1] * kc.shape[2])
+    if gpu_out is not None:
+        acc, lse_err = {}, 0.0
+        for (b, kv), ((ro, rl, rdq, rdk, rdv), _) in done:
+            hs = slice(kv * G, (kv + 1) * G)
             pairs_ = (("o", gpu_out["o"][b, hs], ro), ("dq", gpu_out["dq"][b, hs], rdq),
                       ("dk", gpu_out["dk"][b, kv], rdk), ("dv", gpu_out["dv"][b, kv], rdv))
             for name, got, ref in pairs_:
@@ -139,21 +236,107 @@ def cpu_baseline(w, inputs, budget_s=15.0, gpu_out=None):
                 acc[name][1].append(ref.ravel())
             lse_err = max(lse_err, float(np.abs(gpu_out["lse"][b, hs].double().numpy()
                                                 - rl).max()))
-        if spent >= budget_s:
-            break
-    out = {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-           "kind": "oracle",
-           "sample": f"{done} of {len(groups)} (window, KV head) groups of {w.name} "
-                     f"({G} query heads x {w.chunk_len} rows vs {w.prefix_len + w.chunk_len} "
-                     f"keys each), fp64 forward + backward, {spent:.1f} s"}
-    if gpu_out is not None:
         err = {}
         for name, (a, r) in acc.items():
             a, r = np.concatenate(a), np.concatenate(r)
             err[name] = float(np.linalg.norm(a - r) / np.linalg.norm(r))
         err["lse_abs"] = lse_err
         out["parity_vs_gpu"] = {k: round(v, 6) for k, v in err.items()}
-        out["parity_vs_gpu"]["groups"] = done
+        out["parity_vs_gpu"]["groups"] = n
+    return out
+
+
+class StepSetup:
+    """Device buffers and the calls of one chunk step of workload w: the prefix cache
+    built by one append of the raw rows, then chunk_attn_fwd_append (forward and the
+    append of the chunk's K/V to cache rows [P, P + C), one launch: the backward reads
+    cache rows [0, P) only, so the step's outputs are those of forward, backward, then
+    append) and chunk_attn_bwd."""
+
+    def __init__(self, pka, w, inputs, dev):
+        import torch
+        d = {k: v.to(dev) for k, v in inputs.items()}
+        B, Hq, Hkv, D, P, C = (w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, w.prefix_len,
+                               w.chunk_len)
+        self.cache = pka.PrefixCache.empty(w.cache_type, B, Hkv, P + C, D, dev)
+        if P > 0:
+            pka.kv_append(d["kp"], d["vp"], self.cache, 0)
+        del d["kp"], d["vp"]
+        self.q, self.kc, self.vc, self.do = d["q"], d["kc"], d["vc"], d["do"]
+        sc = w.softmax_scale
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
+        self.dq = torch.empty_like(self.q)
+        self.dk, self.dv = torch.empty_like(self.kc), torch.empty_like(self.vc)
+        dims = pka.make_dims(B, Hq, Hkv, D, P, C, sc)
+        wsf, wsb = pka.fwd_workspace_bytes(dims), pka.bwd_workspace_bytes(dims)
+        self.ws_f = torch.empty(wsf, dtype=torch.uint8, device=dev) if wsf else None
+        self.ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        q, kc, vc, do, o, lse, cache = self.q, self.kc, self.vc, self.do, self.o, self.lse, \
+            self.cache
+        dq, dk, dv, ws_f, ws_b = self.dq, self.dk, self.dv, self.ws_f, self.ws_b
+
+        def fwd_append():
+            pka.chunk_attn_fwd_append(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
+
+        def bwd():
+            pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, dq=dq, dk=dk, dv=dv,
+                               ws=ws_b)
+
+        def step():
+            fwd_append()
+            bwd()
+
+        self.fwd_append, self.bwd, self.step = fwd_append, bwd, step
+
+
+def time_workloads(pka, names, steps, warmup, warmup_ms):
+    """The step of each named workload, timed like the headline (untimed warm-up, then
+    `steps` back-to-back steps between two synchronisations), one after another and
+    after the headline's timed loop. Per workload: ms per step, fwd + bwd algorithmic
+    TFLOP/s and its fraction of the bf16 MFMA peak, prefix-cache GB/s (two reads of
+    the prefix per step) and its fraction of HBM bandwidth, and the per-kernel
+    averages of a short pass with every kernel bracketed by HIP events."""
+    import torch
+    import synthetic
+    out = {}
+    for name in names:
+        w = synthetic.WORKLOAD_BY_NAME[name]
+        st = StepSetup(pka, w, synthetic.make_inputs(w), "cuda:0")
+        warm_up(st.step, warmup, warmup_ms)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        fwd_f, bwd_f, _ = flops(w)
+        tf = (fwd_f + bwd_f) / (ms * 1e-3) / 1e12
+        gbs = 2 * prefix_bytes(w) / (ms * 1e-3) / 1e9
+        pka.profile_reset()
+        pka.profile_select(None)
+        pka.profile_enable(True)
+        for _ in range(min(steps, 20)):
+            st.step()
+        torch.cuda.synchronize()
+        pka.profile_enable(False)
+        kern = {}
+        for k in ("fwd", "fwd_combine", "bwd_dq", "bwd_dkdv", "bwd_dq_reduce"):
+            tot, n, _ = pka.profile_read(k)
+            if n:
+                kern[k] = round(tot / n, 5)
+        out[name] = {"ms_per_step": round(ms, 5), "tflops": round(tf, 2),
+                     "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "prefix_kv_gbs": round(gbs, 1),
+                     "prefix_kv_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "flop_per_step": fwd_f + bwd_f, "steps": steps,
+                     "config": {"batch": w.batch, "n_heads_q": w.n_heads_q,
+                                "n_heads_kv": w.n_heads_kv, "head_dim": w.head_dim,
+                                "prefix_len": w.prefix_len, "chunk_len": w.chunk_len,
+                                "cache": w.cache_type},
+                     "kernel_ms": kern}
+        del st
+        torch.cuda.empty_cache()
     return out
 
 
@@ -418,6 +601,9 @@ def main():
     ap.add_argument("--row-sparse", type=float, default=0.5, metavar="FRAC",
                     help="kept fraction for timing the row-sparse linear backward of one "
                          "1.7B-class layer's projections at 2048 tokens (< 0: skip)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other four workloads' steps (the `configs` "
+                         "object, after the headline's timed loop)")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the prefix-gradient, decode and row-sparse legs")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -448,34 +634,11 @@ def main():
     w = synthetic.WORKLOAD_BY_NAME[args.workload]
     dev = "cuda:0"
     inputs = synthetic.make_inputs(w)
-    d = {k: v.to(dev) for k, v in inputs.items()}
+    st = StepSetup(pka, w, inputs, dev)
     B, Hq, Hkv, D, P, C = w.batch, w.n_heads_q, w.n_heads_kv, w.head_dim, w.prefix_len, w.chunk_len
-    cache = pka.PrefixCache.empty(w.cache_type, B, Hkv, P + C, D, dev)
-    pka.kv_append(d["kp"], d["vp"], cache, 0)
-    del d["kp"], d["vp"]
-    q, kc, vc, do = d["q"], d["kc"], d["vc"], d["do"]
-    sc = w.softmax_scale
-    o = torch.empty_like(q)
-    lse = torch.empty((B, Hq, C), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(kc), torch.empty_like(vc)
-    dims = pka.make_dims(B, Hq, Hkv, D, P, C, sc)
-    wsf = pka.fwd_workspace_bytes(dims)
-    wsb = pka.bwd_workspace_bytes(dims)
-    ws_f = torch.empty(max(wsf, 1), dtype=torch.uint8, device=dev) if wsf else None
-    ws_b = torch.empty(wsb, dtype=torch.uint8, device=dev)
-
-    # The forward and the append of the chunk's K/V to cache rows [P, P + C) run as one
-    # launch (pka_chunk_attn_fwd_append): the backward reads cache rows [0, P) only, so
-    # the step's outputs are those of forward, backward, then append.
-    def fwd_append():
-        pka.chunk_attn_fwd_append(q, kc, vc, cache, P, sc, o=o, lse=lse, ws=ws_f)
-
-    def bwd():
-        pka.chunk_attn_bwd(q, kc, vc, cache, P, sc, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws_b)
-
-    def step():
-        fwd_append()
-        bwd()
+    q, kc, vc, do, o, lse, dq, dk, dv, cache = (st.q, st.kc, st.vc, st.do, st.o, st.lse, st.dq,
+                                                st.dk, st.dv, st.cache)
+    fwd_append, bwd, step = st.fwd_append, st.bwd, st.step
 
     warm = warm_up(step, args.warmup, args.warmup_ms)
 
@@ -563,6 +726,17 @@ def main():
         except Exception as e:  # noqa: BLE001
             out[name] = {"error": f"{type(e).__name__}: {e}"}
 
+    if not args.no_configs:
+        others = [x.name for x in synthetic.WORKLOADS if x.name != w.name]
+        leg("configs", lambda: time_workloads(pka, others, args.steps, args.warmup,
+                                              min(args.warmup_ms, 150.0)))
+        if isinstance(out.get("configs"), dict) and "error" not in out["configs"]:
+            out["configs"][w.name] = {"ms_per_step": round(ms_step, 5),
+                                      "tflops": round(tflops, 2),
+                                      "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                                      "prefix_kv_gbs": round(prefix_gbs, 1),
+                                      "prefix_kv_hbm_frac": round(prefix_gbs / PEAK_HBM_GBS, 4),
+                                      "headline": True}
     if not args.no_next and args.prefix_horizon > 0:
         leg("prefix_kv_grad", lambda: time_prefix_kv_grad(
             pka, w, dict(q=q, kc=kc, vc=vc, o=o, lse=lse, do=do), cache, args.prefix_horizon,

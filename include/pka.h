@@ -5,11 +5,12 @@
  *  - "Context-Frozen Training", The Solution: a no-grad forward of the context builds
  *    its KV cache (Phase 1); the decision tokens then run forward and backward against
  *    that frozen cache (Phase 2); gradients flow through the decision tokens only.
- *  - "train: walk the window" (llama.cpp), What it is / Contents: each reply chunk is
- *    trained against the cached prefix, which it reads as constants stored at F16 or
- *    q8_0; the chunk is then re-decoded into the cache so the next chunk sees it.
- *    Approval comment: V is cached untransposed (so it can be quantised) and the cache
- *    type should follow the serving context, i.e. it is a call argument here.
+ *  - "train: walk the window" (llama.cpp), What it is / Contents: a window is trained
+ *    one chunk at a time; each chunk reads the earlier tokens from a KV cache that is
+ *    held fixed (F16 or q8_0 storage), and after its step the chunk's own K/V are
+ *    written into that cache for the chunks after it. Approval comment: V is kept in
+ *    token-major order, not transposed, which is what lets it be block-quantised, and
+ *    the storage type is whatever the serving side uses, so here it is an argument.
  *  - "stop-gradient through context tokens" (prime-rl), Known gaps: an attention
  *    backward that produces gradient for the kept (chunk) queries only.
  *
@@ -142,8 +143,9 @@ pka_status pka_chunk_attn_fwd_append(const pka_dims* dims, const void* q, const 
  *   dk = scale * dS^T q,  dv = P^T d_o   for the chunk's own C keys only,
  * with P = exp(scale q K^T - lse) (masked) and dS = P * (d_o V^T - delta); dk, dv
  * are summed over the G query heads of each KV head. The prefix gets no gradient:
- * its rows are stop-gradient constants ("train: walk the window", Why it's a draft;
- * "stop-gradient through context tokens", Known gaps: grad for kept queries only).
+ * its rows are fixed inputs of the step ("train: walk the window", Why it's a draft;
+ * "stop-gradient through context tokens", Known gaps: gradient for the kept queries
+ * alone).
  * o and lse are the forward's outputs. delta (f32 [B][Hq][C]) is written if not
  * NULL. ws: pka_bwd_workspace_bytes(dims) bytes (always > 0). */
 pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k,

@@ -17,10 +17,10 @@ What is computed (the plain definition; no blocking, no online softmax):
 * Backward from an upstream dO on the chunk rows only: Delta_i = dO_i . O_i,
   dPr = dO Vf^T, dS = Pr * (dPr - Delta), dQ = scale dS Kf,
   dKc = scale dS[:, P:]^T Q and dVc = Pr[:, P:]^T dO summed over the G query heads of
-  the KV head. The prefix rows get no gradient at all: they are stop-gradient
-  constants ("train: walk the window", Why it's a draft: cached prefixes are
-  stop-gradient constants; "stop-gradient through context tokens", Known gaps: a
-  query-split attention backward produces gradient for kept queries only).
+  the KV head. The prefix rows get no gradient at all: the cache is a fixed input
+  of the step ("train: walk the window", Why it's a draft; "stop-gradient through
+  context tokens", Known gaps: an attention backward split by query that gives
+  gradient to the kept queries alone).
 
 The full-window functions (plain causal attention over L tokens, every row a query)
 exist only to check the invariants that tie the chunk form to ordinary attention.

@@ -1,8 +1,8 @@
 """Oracle of the prefix-cache storage conversions (test infrastructure only).
 
-The cached context is held as constants in F16 or q8_0 ("train: walk the window",
-Contents: cache constants at F16 or q8_0; approval comment: the cache type should
-follow the serving context, and V is cached untransposed so it can be quantised).
+The cached context is held fixed, in F16 or q8_0 storage ("train: walk the window",
+Contents; approval comment: the storage type is the serving side's, and V is kept
+token-major rather than transposed, which is what allows block quantisation of it).
 A bf16 cache (a plain copy of the bf16 rows) is also supported.
 
 q8_0 is named on that page but not spelled out. It is read here as the ggml Q8_0
@@ -109,7 +109,8 @@ def build_prefix(x: np.ndarray, cache_type: str) -> dict:
 def append_rows(x: np.ndarray, cache_type: str) -> dict:
     """The cache rows [P, P+C) an append of the chunk's K or V writes.
 
-    The chunk is re-decoded into the cache so the next chunk sees it ("train: walk
-    the window", What it is); the stored form is the cache's own type.
+    After its step a chunk's K/V are written into the cache, where the following
+    chunks read them ("train: walk the window", What it is); the stored form is the
+    cache's own type.
     """
     return build_prefix(x, cache_type)

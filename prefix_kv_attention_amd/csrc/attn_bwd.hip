@@ -2,10 +2,10 @@
 //
 // Gradient flows through the chunk only: dQ for the chunk's query rows over every
 // key they read (cache and chunk), and dK/dV for the chunk's own C keys. The cached
-// rows are stop-gradient constants and get nothing ("Context-Frozen Training",
-// The Gradient Signal; "train: walk the window", Why it's a draft: cached prefixes
-// are stop-gradient constants; "stop-gradient through context tokens", Known gaps:
-// an attention backward that computes gradient for the kept queries only).
+// rows are fixed inputs with no gradient path and receive nothing ("Context-Frozen
+// Training", The Gradient Signal; "train: walk the window", Why it's a draft;
+// "stop-gradient through context tokens", Known gaps: the attention backward is to
+// produce gradient for the kept queries alone).
 //
 // Kernels, in launch order on the caller's stream:
 //  1. bwd_dq:    delta_i = sum_d dO_id * O_id from the stored bf16 O (prologue; the

@@ -1,9 +1,9 @@
 // Cache writes and the q8_0 dequantisation hook, gfx950.
 //
-// After a chunk is trained it is re-decoded into the cache so the next chunk reads
-// it as part of the frozen prefix ("train: walk the window", What it is). The cache
-// holds F16 or q8_0 constants (same page, Contents) and V is cached untransposed so
-// it can be quantised along head_dim (approval comment). bf16 caches are a copy.
+// Once a chunk's step is done its K/V rows are written into the cache, and later
+// chunks read them as part of the fixed prefix ("train: walk the window", What it
+// is). The storage is F16 or q8_0 (same page, Contents); V is token-major like K,
+// so its blocks of 32 run along head_dim (approval comment). bf16 caches are a copy.
 //
 // The q8_0 block format and the conversions are in pka_device.hpp (q8_0_block,
 // to_cache16); the fused forward + append of attn_fwd.hip uses the same functions.
@@ -40,23 +40,18 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(DequantParams p) {
   const int64_t bh = orow / p.rows, r = orow % p.rows;
   const int64_t crow = bh * p.cap + p.row0 + r;
   const int8_t* src = (is_v ? p.cv : p.ck) + crow * p.D + c8 * 8;
-  const float d = f16_to_f32((is_v ? p.cvs : p.cks)[crow * (p.D / 32) + c8 / 4]);
   const u32x2 c = *reinterpret_cast<const u32x2*>(src);
+  RawRow8 raw;
+  raw.w = u32x4{c.x, c.y, (uint32_t)(is_v ? p.cvs : p.cks)[crow * (p.D / 32) + c8 / 4], 0u};
+  // The same conversion the attention kernels apply when they stage a q8_0 tile:
+  // dequant8_q8_0, and for the bf16 output to_bf16x8 (the MFMA operand bits).
   float x[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t w = e < 4 ? c.x : c.y;
-    x[e] = d * (float)(int8_t)((w >> (8 * (e & 3))) & 0xff);
-  }
+  dequant8_q8_0(raw, x);
   const int64_t out = (is_v ? n * 8 : 0) + orow * p.D + c8 * 8;
   f32x4* of = reinterpret_cast<f32x4*>(p.out_f32 + out);
   of[0] = f32x4{x[0], x[1], x[2], x[3]};
   of[1] = f32x4{x[4], x[5], x[6], x[7]};
-  if (p.out_bf16) {
-    u32x4 o = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
-               pack_bf16(x[6], x[7])};
-    *reinterpret_cast<u32x4*>(p.out_bf16 + out) = o;
-  }
+  if (p.out_bf16) *reinterpret_cast<u32x4*>(p.out_bf16 + out) = to_bf16x8<kQ8>(raw, true);
 }
 
 }  // namespace

@@ -88,7 +88,22 @@ __device__ __forceinline__ bool load_row8(RawRow8& r, const void* cache_base,
   return false;
 }
 
+// q8_0 dequantisation of 8 codes of one block: x = f32(d16) * q, the product of an
+// 11-bit and an 8-bit significand, so exact in fp32 (an infinite scale gives +-inf,
+// and NaN for a zero code, as the plain product does). The attention kernels and the
+// dequantisation hook both call this one function. r.w.x / r.w.y hold the 8 code
+// bytes (value e in byte e % 4 of word e / 4), r.w.z the block's fp16 scale bits.
+__device__ __forceinline__ void dequant8_q8_0(const RawRow8& r, float (&x)[8]) {
+  const float d = f16_to_f32(r.w.z & 0xffffu);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w = e < 4 ? r.w.x : r.w.y;
+    x[e] = d * (float)(int8_t)((w >> (8 * (e & 3))) & 0xffu);
+  }
+}
+
 // Raw row -> 8 bf16 values packed in 4 dwords (element 2i in the low half of .i).
+// F16 and q8_0 values are converted to fp32 exactly, then rounded to bf16 (RNE).
 template <int CT>
 __device__ __forceinline__ u32x4 to_bf16x8(const RawRow8& r, bool is_cache) {
   if (!is_cache || CT == kBF16) return r.w;
@@ -101,23 +116,10 @@ __device__ __forceinline__ u32x4 to_bf16x8(const RawRow8& r, bool is_cache) {
     }
     return o;
   } else {
-    // d * q exactly: with u = q + 128 in [1, 255] (flip the sign bit of each byte),
-    // d*u is exact in fp32 (11 + 8 significant bits) and fma(d, u, -128 d) rounds
-    // the exact d*q once, which is representable -- so this equals fl32(d * q) while
-    // each value costs one unsigned-byte conversion and one fma.
-    const float d = f16_to_f32(r.w.z);
-    const float nd = -128.f * d;
-    const uint32_t x = r.w.x ^ 0x80808080u, y = r.w.y ^ 0x80808080u;
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t w = (i < 2) ? x : y;
-      const int sh = (i & 1) * 16;
-      const float a = fmaf(d, (float)((w >> sh) & 0xffu), nd);
-      const float b = fmaf(d, (float)((w >> (sh + 8)) & 0xffu), nd);
-      o[i] = pack_bf16(a, b);
-    }
-    return o;
+    float x[8];
+    dequant8_q8_0(r, x);
+    return u32x4{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]),
+                 pack_bf16(x[6], x[7])};
   }
 }
 

@@ -108,6 +108,64 @@ def compare_groups(case: Case, groups, o, lse, dq, dk, dv, delta=None):
     return out
 
 
+def sample_groups(case: Case, n: int = 4):
+    """n (window, KV head) groups spread over the batch: the first, the last and
+    interior ones (all of them when there are at most n)."""
+    groups = case.all_groups()
+    if len(groups) <= n:
+        return groups
+    idx = sorted({round(k * (len(groups) - 1) / (n - 1)) for k in range(n)})
+    return [groups[i] for i in idx]
+
+
+def compare_groups_bounded(case: Case, groups, o, lse, dq, dk, dv):
+    """As compare_groups, plus the worst per-(window, head) relative L2, the worst
+    per-row relative L2, and the largest ratio of an element's error to its
+    first-order rounding bound (tests/_bounds.py; parity needs ratio <= 1)."""
+    from _bounds import group_reference_and_bounds, ratio, row_rel_l2
+    G = case.w.group
+    sc = case.w.softmax_scale
+    kpv, vpv = case.oracle_prefix()
+    acc = {k: ([], []) for k in ("o", "dq", "dk", "dv")}
+    worst_head = {k: 0.0 for k in acc}
+    worst_row = {k: 0.0 for k in acc}
+    worst_ratio = {k: 0.0 for k in ("o", "lse", "dq", "dk", "dv")}
+    lse_err = 0.0
+    for b, kv in groups:
+        hs = slice(kv * G, (kv + 1) * G)
+        ref, bnd = group_reference_and_bounds(
+            f64(case.cpu["q"][b, hs]), f64(case.cpu["kc"][b, kv]), f64(case.cpu["vc"][b, kv]),
+            kpv[b, kv], vpv[b, kv], sc, f64(case.cpu["do"][b, hs]),
+            prefix_rounded=case.w.cache_type != "bf16")
+        got = {"o": f64(o[b, hs]), "dq": f64(dq[b, hs]), "dk": f64(dk[b, kv]),
+               "dv": f64(dv[b, kv]), "lse": f64(lse[b, hs])}
+        for name in acc:
+            acc[name][0].append(got[name].ravel())
+            acc[name][1].append(ref[name].ravel())
+            heads = [(got[name], ref[name])] if name in ("dk", "dv") else \
+                [(got[name][g], ref[name][g]) for g in range(G)]
+            for gg, rr in heads:
+                worst_head[name] = max(worst_head[name], rel_l2(gg, rr))
+            worst_row[name] = max(worst_row[name], row_rel_l2(got[name], ref[name]))
+        for name in worst_ratio:
+            worst_ratio[name] = max(worst_ratio[name], ratio(got[name], ref[name], bnd[name]))
+        lse_err = max(lse_err, float(np.abs(got["lse"] - ref["lse"]).max()))
+    out = {k: rel_l2(np.concatenate(a), np.concatenate(r)) for k, (a, r) in acc.items()}
+    out["lse_abs"] = lse_err
+    out["worst_head_rel_l2"] = worst_head
+    out["worst_row_rel_l2"] = worst_row
+    out["bound_ratio"] = worst_ratio
+    out["groups"] = [list(g) for g in groups]
+    return out
+
+
+def assert_bounded(errs: dict, label: str):
+    """Stated bars on the sampled groups, and every element within its bound."""
+    assert_within(errs, label)
+    bad = {k: v for k, v in errs["bound_ratio"].items() if not v <= 1.0}
+    assert not bad, f"{label}: elements outside their rounding bound {bad} (all: {errs})"
+
+
 # Tolerances: relative L2 1e-2 for O and 2e-2 for dQ/dK/dV (bf16 operands, fp32
 # accumulation); LSE feeds the backward, so it is gated at 5e-3 absolute.
 TOL = dict(o=1e-2, dq=2e-2, dk=2e-2, dv=2e-2, delta=2e-2, lse_abs=5e-3)
