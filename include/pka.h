@@ -154,6 +154,24 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
                               void* dv, float* delta, void* ws, size_t ws_bytes,
                               pka_stream_t stream);
 
+/* pka_chunk_attn_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * training loops, harnesses that forbid hipMalloc. The workspace is a fixed array of
+ * PKA_BWD_NOALLOC_MAX_WORKSPACE bytes inside the library, one per GPU, held by that GPU
+ * from the first call on it until the process ends. Outputs and every other argument
+ * are as in pka_chunk_attn_bwd (same kernels, same results bit for bit).
+ * Errors: PKA_ERR_WORKSPACE (nothing launched) when pka_bwd_workspace_bytes(dims)
+ * exceeds that size; the other statuses as pka_chunk_attn_bwd.
+ * Concurrency: all calls on one GPU share its array, so two of them in flight at the
+ * same time (on different streams, or from different threads without ordering) race
+ * and give wrong results; order them on one stream. The array keeps what the last
+ * call left in it; no call depends on its contents. */
+#define PKA_BWD_NOALLOC_MAX_WORKSPACE ((size_t)96 << 20)
+pka_status pka_chunk_attn_bwd_noalloc(const pka_dims* dims, const void* q, const void* k,
+                                      const void* v, const pka_cache* cache, const void* o,
+                                      const float* lse, const void* d_o, void* dq, void* dk,
+                                      void* dv, float* delta, pka_stream_t stream);
+
 /* Gradient of the chunk's loss with respect to the last `horizon` cached prefix rows
  * of every window, from the chunk's queries only: the part of the exact reverse pass
  * that a stop-gradient prefix drops ("train: walk the window", Why it's a draft: an

@@ -6,12 +6,13 @@ provides device memory and the current HIP stream. Importing this package raises
 if the library is missing; there is no fallback implementation.
 
 Names follow the C entry points of include/pka.h without the ``pka_`` prefix:
-``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``, ``kv_append_q8_0``,
+``chunk_attn_fwd``, ``chunk_attn_fwd_append``, ``chunk_attn_bwd``,
+``chunk_attn_bwd_noalloc``, ``kv_append_q8_0``,
 ``kv_append_f16``, ``kv_append_bf16``, ``kv_dequant_q8_0``, ``prefix_kv_grad``,
 ``fwd_workspace_bytes``, ``bwd_workspace_bytes``, ``prefix_kv_grad_workspace_bytes``,
 ``row_sparse_linear_bwd``, ``row_sparse_workspace_bytes``, ``profile_*``. ``chunk_attention`` wraps forward and backward in an
-autograd function whose cache inputs get no gradient (they are stop-gradient
-constants: "train: walk the window", Why it's a draft). ``WindowWalk`` drives the
+autograd function whose cache inputs get no gradient (the cache is a fixed input:
+"train: walk the window", Why it's a draft). ``WindowWalk`` drives the
 chunk loop of a batch of windows: step, append, advance every window's prefix.
 
 Every call takes ``prefix_len`` (an int: the prefix of every window, or the
@@ -76,6 +77,8 @@ _SIGS = {
                                                  _vp, _vp, _sz, _vp]),
     "pka_chunk_attn_bwd": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp, _vp,
                                           _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pka_chunk_attn_bwd_noalloc": (ctypes.c_int, [_P(Dims), _vp, _vp, _vp, _P(CacheDesc), _vp,
+                                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "pka_prefix_kv_grad_workspace_bytes": (_sz, [_P(Dims), _i64]),
     "pka_prefix_kv_grad": (ctypes.c_int, [_P(Dims), _i64, _vp, _P(CacheDesc), _vp, _vp, _vp,
                                           _vp, _vp, _vp, _sz, _vp]),
@@ -303,6 +306,33 @@ def chunk_attn_bwd(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta), _ptr(ws),
                                    nws, _stream(q.device)),
            "pka_chunk_attn_bwd")
+    return dq, dk, dv
+
+
+# Size of the library's own backward workspace (pka.h: PKA_BWD_NOALLOC_MAX_WORKSPACE).
+BWD_NOALLOC_MAX_WORKSPACE = 96 << 20
+
+
+def chunk_attn_bwd_noalloc(q, k, v, cache: PrefixCache, prefix_len: int, scale: float, o,
+                           lse, d_o, dq, dk, dv, delta=None, prefix_lens=None):
+    """chunk_attn_bwd through pka_chunk_attn_bwd_noalloc: the caller passes every output
+    and the library uses its own fixed per-GPU workspace, so the call allocates nothing
+    (usable under graph capture). Calls on one GPU must not overlap in time."""
+    dims = _chunk_inputs(q, k, v, cache, prefix_len, scale, prefix_lens)
+    _tensor(o, "o", q.shape, torch.bfloat16, q.device)
+    _tensor(d_o, "d_o", q.shape, torch.bfloat16, q.device)
+    _tensor(lse, "lse", q.shape[:3], torch.float32, q.device)
+    _tensor(dq, "dq", q.shape, torch.bfloat16, q.device)
+    _tensor(dk, "dk", k.shape, torch.bfloat16, q.device)
+    _tensor(dv, "dv", k.shape, torch.bfloat16, q.device)
+    if delta is not None:
+        _tensor(delta, "delta", q.shape[:3], torch.float32, q.device)
+    cd = cache.desc()
+    _check(_lib.pka_chunk_attn_bwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                           ctypes.byref(cd), _ptr(o), _ptr(lse), _ptr(d_o),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(delta),
+                                           _stream(q.device)),
+           "pka_chunk_attn_bwd_noalloc")
     return dq, dk, dv
 
 

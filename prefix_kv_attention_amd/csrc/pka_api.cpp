@@ -419,6 +419,59 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
   return PKA_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free bwd
+// The backward's workspace in device memory that the library owns: one file-scope
+// array per GPU, which that GPU holds until the process ends. In host code `scratch`
+// names a host-side stand-in, never the device memory, so its device address is looked
+// up once per device (with that device current) and only that address is used.
+namespace {
+constexpr size_t kScratchBytes = PKA_BWD_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pka_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKA_ERR_UNSUPPORTED, "device %d beyond the %d the library supports", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKA_OK;
+}
+}  // namespace
+
+pka_status pka_chunk_attn_bwd_noalloc(const pka_dims* dims, const void* q, const void* k,
+                                      const void* v, const pka_cache* cache, const void* o,
+                                      const float* lse, const void* d_o, void* dq, void* dk,
+                                      void* dv, float* delta, pka_stream_t stream) {
+  g_last_error[0] = 0;
+  pka_status st;
+  if ((st = check_dims(dims)) != PKA_OK) return st;
+  const size_t need = pka_bwd_workspace_bytes(dims);
+  if (need > kScratchBytes)
+    return fail(PKA_ERR_WORKSPACE,
+                "chunk_attn_bwd_noalloc: this shape needs %zu workspace bytes, above the "
+                "library's fixed %zu (use pka_chunk_attn_bwd with a caller workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != PKA_OK) return st;
+  // Same validation, plan and kernels as the call with a caller workspace. Nothing in
+  // the workspace needs to start at zero: every byte the kernels read (delta, split
+  // partials) is written earlier in the same call.
+  return pka_chunk_attn_bwd(dims, q, k, v, cache, o, lse, d_o, dq, dk, dv, delta, ws,
+                            kScratchBytes, stream);
+}
+
 static pka_status check_horizon(const pka_dims* dims, int64_t horizon) {
   if (horizon < 0 || horizon > dims->prefix_len)
     return fail(PKA_ERR_DIMS, "horizon %lld outside [0, prefix_len = %lld]", (long long)horizon,
