@@ -17,20 +17,28 @@
 //  * O^T += V^T P^T: the S^T registers (converted to bf16) are the B operand as is;
 //    the V^T operand is read from the row-major V tile with the transposing LDS
 //    read, so no transposed copy is ever staged.
+//  * Ping-pong of the two waves of each SIMD: waves 0-3 and 4-7 run the same sequence
+//    of phases, one phase apart, with a workgroup barrier between phases. A phase of
+//    one wave is either its MFMA block (S of tile i, P V of tile i - 1) or its VALU
+//    block (the online softmax of tile i, and staging). So while one wave of a SIMD
+//    keeps the matrix core busy, the other's exp2 / fma / pack work runs beside it
+//    instead of after it (measured with a register-only model of the tile: 2,100
+//    cycles per tile against 2,066 for the MFMAs alone and 2,593 when each wave runs
+//    its MFMAs and its VALU work back to back).
 //  * The key sequence [cache rows ; chunk rows] is streamed in 64-key tiles through
-//    two LDS buffers (one barrier per tile). Tiles that lie wholly in the cache use
-//    a fast path (uniform base pointer, fixed per-thread offsets); F16 / q8_0 rows
-//    are converted to bf16 while staging (dequantised on load). Only tiles that
-//    cross the causal diagonal are masked.
+//    two LDS buffers per tensor; waves 0-3 stage the K tiles and waves 4-7 the V tiles,
+//    each in its own VALU phase, loading one phase pair ahead. Tiles that lie wholly
+//    in the cache use a fast path (uniform base pointer, fixed per-thread offsets);
+//    F16 / q8_0 rows are converted to bf16 while staging (dequantised on load). Only
+//    tiles that cross the causal diagonal are masked.
 //  * The probabilities of a tile are taken against the running reference max; the
 //    reference is raised to the exact row max (and the accumulator rescaled) only
 //    when it is unset or a lane's partial row sum of the tile exceeds 2^8, which any
 //    probability above 2^8 forces. So the max reduction and the rescale are skipped
 //    on almost every tile, and probabilities stay <= 2^8, which bf16 and fp32 hold
 //    exactly enough. The result is the same softmax (any reference max gives it).
-//  * LDS operand reads run several MFMAs ahead of their use (sched_ahead), the two
-//    32-key S chains of a tile interleave, and the first P V operands are read before
-//    the softmax: without that the wave waits out the LDS latency at each MFMA.
+//  * LDS operand reads run several MFMAs ahead of their use (sched_chain2): without
+//    that the wave waits out the LDS latency at each MFMA.
 //  * With FwdParams::append the same launch writes the chunk's K/V into the cache
 //    rows [P_b, P_b + C) after its last tile (the re-decode into the cache).
 //  * When (window, KV head, row block) units are too few to fill 256 CUs, the key
@@ -46,7 +54,11 @@ namespace {
 constexpr int BN = kKeysPerTile;   // keys per tile
 constexpr int NW = kWavesPerBlock; // waves per workgroup
 constexpr int NTHR = 64 * NW;
-constexpr float kSumLimit = 256.f;  // bound on a lane's partial row sum of one tile
+// Largest probability a tile may produce before the reference max is raised: 2^8
+// (bf16 bits 0x4380); any larger value is exact enough in bf16 and fp32 but could, if
+// left unchecked, grow past what the sums hold.
+constexpr uint16_t kProbLimitBits = 0x4380;
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct FwdLds {
@@ -101,8 +113,17 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
       qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
   }
 
+  // Ping-pong: waves 0-3 (group 0, one per SIMD) and waves 4-7 (group 1) run the same
+  // phases one phase apart, so on every SIMD one wave issues its MFMA block while the
+  // other runs its softmax VALU and staging; a barrier ends every phase. Group 0
+  // stages the K tiles, group 1 the V tiles.
+  const int grp_w = __builtin_amdgcn_readfirstlane(wave) >> 2;
   const int64_t bh = (int64_t)b * p.Hkv + kv;
-  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, P, p.C);
+  TileStager<CT, D, NTHR / 2, 2> stg(tid & (NTHR / 2 - 1), grp_w ? p.cache.v : p.cache.k,
+                                     grp_w ? p.cache.vs : p.cache.ks, grp_w ? p.vc : p.kc, bh,
+                                     p.cache.cap, P, p.C);
+  uint16_t* const own0 = grp_w ? sm.v[0] : sm.k[0];
+  uint16_t* const own1 = grp_w ? sm.v[1] : sm.k[1];
 
   // Per-lane LDS offsets of the MFMA operands.
   const int k_off = prow(l32) * S + hf * 8;   // + kb*32*S + ks*16
@@ -111,30 +132,54 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   f32x16 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  // Row sums on the matrix core: a 32-row block of ones as one more A operand of
+  // O^T += V^T P^T gives, in every register of lane l, sum_j P_lj over the same bf16
+  // probabilities the numerator uses (the VALU row sum with v_dot2c_f32_bf16 ran
+  // several times slower beside the other wave's MFMAs).
+  f32x16 acc_l = f32x16{};
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  float m = -INFINITY;
   float mc = 0.f;                           // m * c, or 0 while m is unset
   const float c = p.scale_log2;
   const int lim = P + t;                    // this row may attend keys 0..lim
 
-  // MFMA blocks run at raised wave priority: when both waves of a SIMD are ready,
-  // the one feeding the matrix core issues first and the other one's softmax VALU
-  // work fills in behind it (measured: a few percent faster than equal priority).
-  auto scores = [&](const uint16_t* kt, f32x16 (&st)[2]) {
+  // MFMA block of a phase: S^T = K Q^T of tile i (16 MFMAs at D = 128, one LDS read
+  // each) and O^T += V^T P^T of tile i - 1 (16 MFMAs, two transposing reads each),
+  // every read issued kFwdReadAhead MFMAs ahead of its MFMA.
+  constexpr int NS = 2 * NKS, NPV = 4 * NDB;
+  auto mblock = [&](auto do_s, auto do_pv, const uint16_t* kt, f32x16 (&st)[2],
+                    const uint16_t* vt, const u32x4 (&pb)[4]) __attribute__((always_inline)) {
+    constexpr bool kS = decltype(do_s)::value, kPV = decltype(do_pv)::value;
     __builtin_amdgcn_s_setprio(1);
-    bf16x8 a[NKS][2];
+    if constexpr (kS) {
+      st[0] = f32x16{};
+      st[1] = f32x16{};
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
+      for (int i = 0; i < NS; ++i) {
+        const int ks = i >> 1, kb = i & 1;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
+        st[kb] = mfma32(a, qreg[ks], st[kb]);
+      }
+    }
+    if constexpr (kPV) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        a[ks][kb] = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
-    st[0] = f32x16{};
-    st[1] = f32x16{};
+      for (int i = 0; i < NPV; ++i) {
+        const bf16x8 a = lds_tr_operand<S>(vt, v_off, (i / NDB) * 16, (i % NDB) * 32);
+        acc[i % NDB] = mfma32(a, __builtin_bit_cast(bf16x8, pb[i / NDB]), acc[i % NDB]);
+      }
+    }
+    sched_chain2<kS ? NS : 0, 1, kPV ? NPV : 0, 2, kFwdReadAhead>();
+    if constexpr (kPV) {
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) st[kb] = mfma32(a[ks][kb], qreg[ks], st[kb]);
-    sched_ahead<2 * NKS, kFwdReadAhead, 1>();
+      for (int s4 = 0; s4 < 4; ++s4) acc_l = mfma32(ones, __builtin_bit_cast(bf16x8, pb[s4]), acc_l);
+    }
     __builtin_amdgcn_s_setprio(0);
+    if constexpr (kS) {
+      pin(st[0]);
+      pin(st[1]);
+    }
   };
   // Online softmax of one tile. The probabilities are taken against the running
   // reference m first; the exact row max is needed only when that reference is
@@ -142,22 +187,46 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   // kSumLimit whenever some probability does. Then m is raised to the row max,
   // the accumulator rescaled and the tile's probabilities recomputed. Returns the
   // probabilities as the bf16 B operands of P V.
-  auto probs = [&](const f32x16 (&st)[2], bf16x8 (&pb)[4]) {
-    float lt = 0.f;
+  // The VALU block runs alone on its SIMD half the time, so its dependency chains are
+  // not hidden by another wave: the work goes in independent stages (every fma, then
+  // every exp2, then the bf16 packs), each kept apart by a scheduling barrier.
+  // Returns true if some probability of this lane exceeds kProbLimit (bf16 bits of
+  // non-negative values order like unsigned integers).
+  auto probs = [&](const f32x16 (&st)[2], u32x4 (&pb)[4]) __attribute__((always_inline)) {
+    float x[32];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -mc)),
-                                     __builtin_amdgcn_exp2f(fmaf(st[kb][i + 1], c, -mc)));
-        lt = add_bf16_pair(w, lt);
-        const bf16x2 pr = __builtin_bit_cast(bf16x2, w);
-        pb[kb * 2 + (i >> 3)][i & 7] = pr[0];
-        pb[kb * 2 + (i >> 3)][(i & 7) + 1] = pr[1];
-      }
-    return lt;
+      for (int i = 0; i < 16; ++i) x[kb * 16 + i] = fmaf(st[kb][i], c, -mc);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = __builtin_amdgcn_exp2f(x[i]);
+    __builtin_amdgcn_sched_barrier(0);
+    // Word j of the packed probabilities holds scores 2j, 2j + 1 of the lane (x index
+    // kb * 16 + i): word j % 4 of B operand j / 4.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      uint32_t word;   // one v_cvt_pk_bf16_f32 (RNE) per pair, written in place
+      asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(word) : "v"(x[2 * j]), "v"(x[2 * j + 1]));
+      pb[j >> 2][j & 3] = word;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // (Each word is copied to a scalar before the bit_cast: hipcc reads element 0
+    // when __builtin_bit_cast is applied to a subscripted vector element.)
+    u16x2 mx[4];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t word = pb[j >> 2][j & 3];
+      const u16x2 h = __builtin_bit_cast(u16x2, word);
+      mx[j & 3] = j < 4 ? h : __builtin_elementwise_max(mx[j & 3], h);
+    }
+    mx[0] = __builtin_elementwise_max(__builtin_elementwise_max(mx[0], mx[1]),
+                                      __builtin_elementwise_max(mx[2], mx[3]));
+    return (mx[0][0] > kProbLimitBits) || (mx[0][1] > kProbLimitBits);
   };
-  auto softmax = [&](f32x16 (&st)[2], int tile, bf16x8 (&pb)[4]) {
+  auto softmax = [&](f32x16 (&st)[2], int tile, u32x4 (&pb)[4]) __attribute__((always_inline)) {
+    pin(st[0]);
+    pin(st[1]);
     const int kbase = tile * BN;
     if (kbase + BN - 1 > P + t_min) {
       const int rel = lim - kbase - hf * 4;  // key kbase + o + hf*4 allowed iff o <= rel
@@ -167,8 +236,8 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kb][i] = -INFINITY;
     }
-    float lt = probs(st, pb);
-    if (__builtin_amdgcn_ballot_w64(lt > kSumLimit || m == -INFINITY) != 0) {
+    const bool big = probs(st, pb);
+    if (__builtin_amdgcn_ballot_w64(big || m == -INFINITY) != 0) {
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -177,57 +246,69 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
       const float mn = fmaxf(m, pair_max(mt));
       // alpha = 1 for rows that keep their max; 0 for rows leaving -inf.
       const float alpha = (mn == m) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * c);
-      l *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc_l[i] *= alpha;
       m = mn;
       mc = (m == -INFINITY) ? 0.f : m * c;
-      lt = probs(st, pb);
+      probs(st, pb);
     }
-    l += lt;
-  };
-  // P V operands: the first kPre are read before the softmax (they do not depend on
-  // it), the rest kFwdReadAhead MFMAs ahead of their use.
-  constexpr int NPV = 4 * NDB;
-  constexpr int kPre = kFwdPvEarlyReads;
-  auto pv_operand = [&](const uint16_t* vt, int i) __attribute__((always_inline)) {
-    return lds_tr_operand<S>(vt, v_off, (i / NDB) * 16, (i % NDB) * 32);
-  };
-  auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4], bf16x8 (&a)[NPV]) {
-    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = kPre; i < NPV; ++i) a[i] = pv_operand(vt, i);
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) acc[i % NDB] = mfma32(a[i], pb[i / NDB], acc[i % NDB]);
-    sched_ahead_after<NPV, kPre, kFwdReadAhead, 2>();
-    __builtin_amdgcn_s_setprio(0);
+    for (int j = 0; j < 4; ++j) pin(pb[j]);
   };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
 
-  if (tb < te) {
-    stg.issue(tb);
-    stg.store(sm.k[0], sm.v[0]);
-    if (tb + 1 < te) stg.issue(tb + 1);
-    __syncthreads();
+  const int n = te - tb;   // tiles of this workgroup (uniform)
+  // Local tile l's rows are loaded into register slot l % 2 two phase pairs before
+  // they are written to LDS (in the VALU phase of tile l - 1).
+  if (n > 0) {
+    stg.template issue<0>(tb);
+    if (n > 1) stg.template issue<1>(tb + 1);
+    stg.template store<0>(own0);
+    if (n > 2) stg.template issue<0>(tb + 2);
   }
+  phase_barrier();
+  // One wait for every load so far (Q, and the next tiles' rows): without it the
+  // compiler cannot tell at the loop header that Q has arrived, and its waits for Q
+  // inside the MFMA block would also wait for the rows just requested.
   wait_global_loads();
-  for (int tile = tb; tile < te; ++tile) {
-    const int cur = (tile - tb) & 1;
-    f32x16 st[2];
-    scores(sm.k[cur], st);
-    bf16x8 pva[NPV];
-#pragma unroll
-    for (int i = 0; i < kPre; ++i) pva[i] = pv_operand(sm.v[cur], i);
-    bf16x8 pb[4];
-    softmax(st, tile, pb);
-    pv_mfma(sm.v[cur], pb, pva);
-    if (tile + 1 < te) {
-      stg.store(sm.k[cur ^ 1], sm.v[cur ^ 1]);
-      if (tile + 2 < te) stg.issue(tile + 2);
-      __syncthreads();
-    }
+  if (grp_w == 1) phase_barrier();   // group 1 runs one phase behind
+  f32x16 st[2];
+  u32x4 pb[4];
+  // phase pair of tile 0: scores, then softmax (and staging of tile 1)
+  if (n > 0) mblock(T_{}, F_{}, sm.k[0], st, sm.v[0], pb);
+  phase_barrier();
+  if (n > 0) {
+    softmax(st, tb, pb);
+    if (n > 1) stg.template store<1>(own1);
+    if (n > 3) stg.template issue<1>(tb + 3);
   }
+  phase_barrier();
+  // Tiles 1 .. n - 1, two per trip so that the register slots are fixed.
+  auto tile_pair = [&](auto slot, int i) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot)::value;   // slot of tile i + 1 = (i + 1) % 2
+    const int cur = i & 1;
+    mblock(T_{}, T_{}, sm.k[cur], st, sm.v[cur ^ 1], pb);
+    phase_barrier();
+    softmax(st, tb + i, pb);
+    if (i + 1 < n) stg.template store<SL>(cur ? own0 : own1);
+    if (i + 3 < n) stg.template issue<SL>(tb + i + 3);
+    phase_barrier();
+  };
+  int i = 1;
+  for (; i + 1 < n; i += 2) {
+    tile_pair(std::integral_constant<int, 0>{}, i);       // i odd: tile i + 1 in slot 0
+    tile_pair(std::integral_constant<int, 1>{}, i + 1);
+  }
+  if (i < n) tile_pair(std::integral_constant<int, 0>{}, i);
+  // last phase: P V of the last tile
+  if (n > 0) mblock(F_{}, T_{}, sm.k[0], st, sm.v[(n - 1) & 1], pb);
+  phase_barrier();
+  if (grp_w == 0) phase_barrier();   // matches group 1's extra barrier
 
   // Fused re-decode: the workgroups of this (window, KV head) share the append of
   // its chunk rows to cache rows [P_b, P_b + C). Those rows are never read by this
@@ -241,7 +322,7 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
                          p.wvs, crow0);
   }
 
-  const float l_tot = pair_sum(l);
+  const float l_tot = acc_l[0];   // the row sum (both lanes of the row hold it)
   if (!row_ok) return;
   if (SPL == 1) {
     const float inv = 1.f / l_tot;

@@ -362,6 +362,124 @@ struct KVStager {
 
 
 // ---------------------------------------------------------------------------
+// Staging of ONE tensor (K or V) of the key sequence [cache rows 0..P-1 ; chunk rows]
+// in tiles of 64 keys, by NTHR threads (one 4-wave group of a ping-pong workgroup).
+// Thread g takes RPT consecutive rows of one 8-value column chunk. Loads go to one of
+// NSLOT register slots (issue), and are converted and written to LDS later (store),
+// so NSLOT tiles can be in flight; the slot is a template argument so that the
+// registers stay registers.
+template <int CT, int D, int NTHR, int NSLOT = 1>
+struct TileStager {
+  static constexpr int BN = kKeysPerTile;
+  static constexpr int CH = D / 8;                 // 8-value chunks per row
+  static constexpr int RPT = BN * CH / NTHR;       // rows per thread
+  static constexpr int ESZ = (CT == kQ8) ? 1 : 2;
+  static constexpr int S = D + 8;
+  static_assert(RPT >= 1 && BN * CH == RPT * NTHR, "tile does not split evenly");
+
+  const char* cbase;        // this (window, KV head)'s cache rows of the tensor
+  const uint16_t* cscale;   // q8_0 scales or null
+  const uint16_t* chunk;    // the chunk's own rows (bf16 [C][D])
+  int tr0, td0;
+  int64_t P, C;
+  int n_fast;               // tiles [0, n_fast) lie wholly in the cache
+  u32x4 raw[NSLOT][RPT];
+  bool in_cache[NSLOT][RPT];
+
+  __device__ __forceinline__ TileStager(int g, const void* cache_base, const uint16_t* scale_base,
+                                        const uint16_t* chunk_base, int64_t bh, int64_t cap,
+                                        int64_t P_, int64_t C_) {
+    P = P_;
+    C = C_;
+    n_fast = (int)(P_ / BN);
+    tr0 = (g / CH) * RPT;
+    td0 = (g % CH) * 8;
+    cbase = static_cast<const char*>(cache_base) + bh * cap * D * ESZ;
+    cscale = (CT == kQ8) ? scale_base + bh * cap * (D / 32) : nullptr;
+    chunk = chunk_base + bh * C_ * D;
+  }
+
+  // Load this thread's rows of tile `tile` into register slot SL.
+  template <int SL = 0>
+  __device__ __forceinline__ void issue(int tile) {
+    if (tile < n_fast) {
+      const char* base = cbase + (int64_t)tile * BN * D * ESZ;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = tr0 + i;
+        if constexpr (CT == kQ8) {
+          const u32x2 c = *reinterpret_cast<const u32x2*>(base + r * D + td0);
+          const uint32_t sc = cscale[((int64_t)tile * BN + r) * (D / 32) + (td0 >> 5)];
+          raw[SL][i] = u32x4{c.x, c.y, sc, 0u};
+        } else {
+          raw[SL][i] = *reinterpret_cast<const u32x4*>(base + (r * D + td0) * 2);
+        }
+        in_cache[SL][i] = true;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        RawRow8 r;
+        in_cache[SL][i] = load_row8<CT, D>(r, cbase, cscale, chunk, P, C,
+                                           (int64_t)tile * BN + tr0 + i, td0);
+        raw[SL][i] = r.w;
+      }
+    }
+  }
+
+  // Convert the rows of slot SL to bf16 and write them to a row-major LDS tile.
+  template <int SL = 0>
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      RawRow8 r;
+      r.w = raw[SL][i];
+      *reinterpret_cast<u32x4*>(&tile[prow(tr0 + i) * S + td0]) = to_bf16x8<CT>(r, in_cache[SL][i]);
+    }
+  }
+};
+
+// Instruction order of a block of N0 MFMAs whose A operands take R0 LDS reads each,
+// followed by N1 MFMAs taking R1 reads each: every read is issued PF MFMAs before the
+// MFMA that uses it (scheduling-group barriers: 0x008 MFMA, 0x100 LDS read).
+template <int K, int N0, int R0, int N1, int R1, int PF>
+__device__ __forceinline__ void sched_chain2_step() {
+  if constexpr (K < N0 + N1) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int J = K + PF;
+    if constexpr (J < N0 + N1) __builtin_amdgcn_sched_group_barrier(0x100, J < N0 ? R0 : R1, 0);
+    sched_chain2_step<K + 1, N0, R0, N1, R1, PF>();
+  }
+}
+template <int J, int N0, int R0, int N1, int R1, int PF>
+__device__ __forceinline__ void sched_chain2_lead() {
+  if constexpr (J < PF && J < N0 + N1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, J < N0 ? R0 : R1, 0);
+    sched_chain2_lead<J + 1, N0, R0, N1, R1, PF>();
+  }
+}
+template <int N0, int R0, int N1, int R1, int PF>
+__device__ __forceinline__ void sched_chain2() {
+  sched_chain2_lead<0, N0, R0, N1, R1, PF>();
+  sched_chain2_step<0, N0, R0, N1, R1, PF>();
+}
+
+// Phase boundary of a ping-pong workgroup: LDS writes of this phase complete, then
+// every wave of the workgroup meets. Nothing is scheduled across it.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Pin a value at this point of the instruction stream: it must be computed before it
+// and may not be read by anything placed before it (an empty asm that "modifies" it).
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// ---------------------------------------------------------------------------
 // Cache writes of the chunk's K/V rows (re-decode into the cache).
 // q8_0 block (32 consecutive values of one token row along head_dim):
 //   amax = max|x|; d = amax / 127 (IEEE fp32 division; the library is built without
