@@ -17,14 +17,18 @@
 //  * O^T += V^T P^T: the S^T registers (converted to bf16) are the B operand as is;
 //    the V^T operand is read from the row-major V tile with the transposing LDS
 //    read, so no transposed copy is ever staged.
-//  * Ping-pong of the two waves of each SIMD: waves 0-3 and 4-7 run the same sequence
-//    of phases, one phase apart, with a workgroup barrier between phases. A phase of
-//    one wave is either its MFMA block (S of tile i, P V of tile i - 1) or its VALU
-//    block (the online softmax of tile i, and staging). So while one wave of a SIMD
-//    keeps the matrix core busy, the other's exp2 / fma / pack work runs beside it
-//    instead of after it (measured with a register-only model of the tile: 2,100
-//    cycles per tile against 2,066 for the MFMAs alone and 2,593 when each wave runs
-//    its MFMAs and its VALU work back to back).
+//  * Ping-pong of the two waves of each SIMD (bf16 caches, fwd_kernel): waves 0-3 and
+//    4-7 run the same sequence of phases, one phase apart, with a workgroup barrier
+//    between phases. A phase of one wave is either its MFMA block (S of tile i, P V of
+//    tile i - 1) or its VALU block (the online softmax of tile i, and staging). So
+//    while one wave of a SIMD keeps the matrix core busy, the other's exp2 / fma / pack
+//    work runs beside it instead of after it (measured with a register-only model of
+//    the tile: 2,100 cycles per tile against 2,066 for the MFMAs alone and 2,593 when
+//    each wave runs its MFMAs and its VALU work back to back). F16 and q8_0 caches take
+//    fwd_serial_kernel instead, where each wave runs both blocks itself and the tile
+//    staging (with its conversion to bf16) is spread over all eight waves: there the
+//    staging makes the VALU phase longer than the MFMA phase, and the ping-pong was
+//    measured slower (q8_0 at P = 63488: 0.710 ms against 0.662 ms).
 //  * The key sequence [cache rows ; chunk rows] is streamed in 64-key tiles through
 //    two LDS buffers per tensor; waves 0-3 stage the K tiles and waves 4-7 the V tiles,
 //    each in its own VALU phase, loading one phase pair ahead. Tiles that lie wholly
@@ -58,6 +62,7 @@ constexpr int NTHR = 64 * NW;
 // (bf16 bits 0x4380); any larger value is exact enough in bf16 and fp32 but could, if
 // left unchecked, grow past what the sums hold.
 constexpr uint16_t kProbLimitBits = 0x4380;
+constexpr float kSumLimit = 256.f;  // bound on a lane's partial row sum of one tile
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
@@ -357,6 +362,230 @@ __global__ __launch_bounds__(NTHR) void fwd_kernel(FwdParams p) {
   }
 }
 
+// The same forward with each wave running its MFMA and softmax work back to back (no
+// ping-pong): taken for F16 and q8_0 caches, whose conversion on staging makes the
+// VALU phase the longer one, so the ping-pong's MFMA phase would wait on it.
+template <int D, int CT>
+__global__ __launch_bounds__(NTHR) void fwd_serial_kernel(FwdParams p) {
+  __shared__ __align__(16) FwdLds<D> sm;
+  constexpr int S = FwdLds<D>::S;
+  constexpr int NKS = D / 16;   // k-steps over head_dim
+  constexpr int NDB = D / 32;   // 32-row blocks of O^T
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+
+  const int n_rb = p.plan.n_rb, SPL = p.plan.n_split;
+  const int L = xcd_logical_id(blockIdx.x, p.plan.nblk);
+  const int rb = L % n_rb;
+  const int split = (L / n_rb) % SPL;
+  const int grp = L / (n_rb * SPL);
+  const int b = grp / p.Hkv, kv = grp % p.Hkv;
+  const int G = p.G;
+  const int C = (int)p.C;
+  const int P = (int)window_prefix(p.plens, b, p.P);  // this window's prefix
+  const int rows = G * C;
+  constexpr int ROWS = 32 * NW;
+
+  const int r = rb * ROWS + wave * 32 + l32;
+  const bool row_ok = r < rows;
+  const int rr = row_ok ? r : rows - 1;
+  const int t = rr / G;
+  const int h = kv * G + (rr - t * G);
+  const int64_t qrow = ((int64_t)b * p.Hq + h) * C + t;
+
+  const int r_first = rb * ROWS;
+  const int r_last = min(rows - 1, r_first + ROWS - 1);
+  const int t_min = r_first / G, t_max = r_last / G;
+  const int key_end = P + t_max + 1;
+  const int n_tiles = (key_end + BN - 1) / BN;
+  const int tb = (int)((int64_t)split * n_tiles / SPL);
+  const int te = (int)((int64_t)(split + 1) * n_tiles / SPL);
+
+  bf16x8 qreg[NKS];
+  {
+    const uint16_t* qp = p.q + qrow * D + hf * 8;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qreg[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
+  }
+
+  const int64_t bh = (int64_t)b * p.Hkv + kv;
+  KVStager<CT, D, NTHR> stg(tid, p.cache, p.kc, p.vc, bh, P, p.C);
+
+  // Per-lane LDS offsets of the MFMA operands.
+  const int k_off = prow(l32) * S + hf * 8;   // + kb*32*S + ks*16
+  const TrOffsets v_off = tr_lane_offsets<S>(lane);  // + (kb*32 + s*16)*S + db*32
+
+  f32x16 acc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  float mc = 0.f;                           // m * c, or 0 while m is unset
+  const float c = p.scale_log2;
+  const int lim = P + t;                    // this row may attend keys 0..lim
+
+  // MFMA blocks run at raised wave priority: when both waves of a SIMD are ready,
+  // the one feeding the matrix core issues first and the other one's softmax VALU
+  // work fills in behind it (measured: a few percent faster than equal priority).
+  auto scores = [&](const uint16_t* kt, f32x16 (&st)[2]) {
+    __builtin_amdgcn_s_setprio(1);
+    bf16x8 a[NKS][2];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        a[ks][kb] = *reinterpret_cast<const bf16x8*>(&kt[k_off + kb * 32 * S + ks * 16]);
+    st[0] = f32x16{};
+    st[1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) st[kb] = mfma32(a[ks][kb], qreg[ks], st[kb]);
+    sched_ahead<2 * NKS, kFwdReadAhead, 1>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Online softmax of one tile. The probabilities are taken against the running
+  // reference m first; the exact row max is needed only when that reference is
+  // unset or too low, which the tile's partial row sum shows: it exceeds
+  // kSumLimit whenever some probability does. Then m is raised to the row max,
+  // the accumulator rescaled and the tile's probabilities recomputed. Returns the
+  // probabilities as the bf16 B operands of P V.
+  auto probs = [&](const f32x16 (&st)[2], bf16x8 (&pb)[4]) {
+    float lt = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const uint32_t w = pack_bf16(__builtin_amdgcn_exp2f(fmaf(st[kb][i], c, -mc)),
+                                     __builtin_amdgcn_exp2f(fmaf(st[kb][i + 1], c, -mc)));
+        lt = add_bf16_pair(w, lt);
+        const bf16x2 pr = __builtin_bit_cast(bf16x2, w);
+        pb[kb * 2 + (i >> 3)][i & 7] = pr[0];
+        pb[kb * 2 + (i >> 3)][(i & 7) + 1] = pr[1];
+      }
+    return lt;
+  };
+  auto softmax = [&](f32x16 (&st)[2], int tile, bf16x8 (&pb)[4]) {
+    const int kbase = tile * BN;
+    if (kbase + BN - 1 > P + t_min) {
+      const int rel = lim - kbase - hf * 4;  // key kbase + o + hf*4 allowed iff o <= rel
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > rel) st[kb][i] = -INFINITY;
+    }
+    float lt = probs(st, pb);
+    if (__builtin_amdgcn_ballot_w64(lt > kSumLimit || m == -INFINITY) != 0) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, st[kb][i]);
+      const float mn = fmaxf(m, pair_max(mt));
+      // alpha = 1 for rows that keep their max; 0 for rows leaving -inf.
+      const float alpha = (mn == m) ? 1.f : __builtin_amdgcn_exp2f((m - mn) * c);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      m = mn;
+      mc = (m == -INFINITY) ? 0.f : m * c;
+      lt = probs(st, pb);
+    }
+    l += lt;
+  };
+  // P V operands: the first kPre are read before the softmax (they do not depend on
+  // it), the rest kFwdReadAhead MFMAs ahead of their use.
+  constexpr int NPV = 4 * NDB;
+  constexpr int kPre = kFwdPvEarlyReads;
+  auto pv_operand = [&](const uint16_t* vt, int i) __attribute__((always_inline)) {
+    return lds_tr_operand<S>(vt, v_off, (i / NDB) * 16, (i % NDB) * 32);
+  };
+  auto pv_mfma = [&](const uint16_t* vt, const bf16x8 (&pb)[4], bf16x8 (&a)[NPV]) {
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = kPre; i < NPV; ++i) a[i] = pv_operand(vt, i);
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) acc[i % NDB] = mfma32(a[i], pb[i / NDB], acc[i % NDB]);
+    sched_ahead_after<NPV, kPre, kFwdReadAhead, 2>();
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  if (tb < te) {
+    stg.issue(tb);
+    stg.store(sm.k[0], sm.v[0]);
+    if (tb + 1 < te) stg.issue(tb + 1);
+    __syncthreads();
+  }
+  wait_global_loads();
+  for (int tile = tb; tile < te; ++tile) {
+    const int cur = (tile - tb) & 1;
+    f32x16 st[2];
+    scores(sm.k[cur], st);
+    bf16x8 pva[NPV];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i) pva[i] = pv_operand(sm.v[cur], i);
+    bf16x8 pb[4];
+    softmax(st, tile, pb);
+    pv_mfma(sm.v[cur], pb, pva);
+    if (tile + 1 < te) {
+      stg.store(sm.k[cur ^ 1], sm.v[cur ^ 1]);
+      if (tile + 2 < te) stg.issue(tile + 2);
+      __syncthreads();
+    }
+  }
+
+  // Fused re-decode: the workgroups of this (window, KV head) share the append of
+  // its chunk rows to cache rows [P_b, P_b + C). Those rows are never read by this
+  // launch (the chunk's keys come from kc / vc), so the writes race with nothing.
+  if (p.append) {
+    const int nu = n_rb * SPL, u = split * n_rb + rb;
+    const int64_t total = append_items<CT, D>(C);
+    const int64_t crow0 = bh * p.cache.cap + P;
+    for (int64_t it = (int64_t)u * NTHR + tid; it < total; it += (int64_t)nu * NTHR)
+      append_item<CT, D>(it, C, p.kc + bh * C * D, p.vc + bh * C * D, p.wk, p.wv, p.wks,
+                         p.wvs, crow0);
+  }
+
+  const float l_tot = pair_sum(l);
+  if (!row_ok) return;
+  if (SPL == 1) {
+    const float inv = 1.f / l_tot;
+    uint16_t* op = p.o + qrow * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hf * 4;
+        u32x2 w;
+        w.x = pack_bf16(acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv);
+        w.y = pack_bf16(acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + d) = w;
+      }
+    if (hf == 0) p.lse[qrow] = m * p.scale + logf(l_tot);
+  } else {
+    const int64_t nrow = (int64_t)p.B * p.Hq * C;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* wo = p.ws_o + ((int64_t)split * nrow + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hf * 4;
+        f32x4 w = {acc[db][g4 * 4 + 0] * inv, acc[db][g4 * 4 + 1] * inv,
+                   acc[db][g4 * 4 + 2] * inv, acc[db][g4 * 4 + 3] * inv};
+        *reinterpret_cast<f32x4*>(wo + d) = w;
+      }
+    if (hf == 0)
+      p.ws_lse[(int64_t)split * nrow + qrow] =
+          l_tot > 0.f ? m * p.scale + logf(l_tot) : -INFINITY;
+  }
+}
+
 // Merge of prefix splits: LSE = logsumexp_s LSE_s, O = sum_s exp(LSE_s - LSE) O_s,
 // summed in split order.
 template <int D>
@@ -393,7 +622,10 @@ __global__ __launch_bounds__(256) void fwd_combine_kernel(FwdParams p) {
 template <int D, int CT>
 hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   prof_begin(PKA_KERNEL_FWD, s);
-  hipLaunchKernelGGL((fwd_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
+  if constexpr (CT == kBF16)
+    hipLaunchKernelGGL((fwd_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_serial_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
   prof_end(PKA_KERNEL_FWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.plan.n_split == 1) return e;
