@@ -264,8 +264,10 @@ const char* pka_last_error(void);
 typedef enum {
   PKA_KERNEL_FWD = 0,        /* forward tiles (one launch per pka_chunk_attn_fwd) */
   PKA_KERNEL_FWD_COMBINE = 1,/* merge of prefix splits                            */
-  PKA_KERNEL_BWD_PREP = 2,   /* reserved: delta is now computed inside bwd_dq      */
-  PKA_KERNEL_BWD_DQ = 3,     /* dq over prefix and chunk keys                      */
+  PKA_KERNEL_BWD_PREP = 2,   /* delta launch, only when the chunk dk, dv run in the
+                                dq grid (shapes whose dq grid leaves CUs idle)     */
+  PKA_KERNEL_BWD_DQ = 3,     /* dq over prefix and chunk keys (with the chunk dk, dv
+                                when those run in the same grid)                   */
   PKA_KERNEL_BWD_DKDV = 4,   /* chunk-only dk, dv                                  */
   PKA_KERNEL_BWD_DQ_REDUCE = 5, /* sums of dq and dk/dv split partials (one launch) */
   PKA_KERNEL_APPEND = 6,     /* kv_append_*                                        */

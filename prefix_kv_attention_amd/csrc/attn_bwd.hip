@@ -7,7 +7,10 @@
 // "stop-gradient through context tokens", Known gaps: the attention backward is to
 // produce gradient for the kept queries alone).
 //
-// Kernels, in launch order on the caller's stream:
+// Kernels, in launch order on the caller's stream (when the dQ row blocks leave CUs
+// idle and the chunk dK/dV units fit there, see bwd_dq_kv below, the order is instead:
+// bwd_delta, then one grid of dQ row blocks and dK/dV units, then bwd_reduce if the dQ
+// rows are split):
 //  1. bwd_dq:    delta_i = sum_d dO_id * O_id from the stored bf16 O (prologue; the
 //                first split of each row writes it for bwd_dkdv), then per 256
 //                packed query rows (GQA packing as in the forward), stream
@@ -52,8 +55,7 @@ struct DqLds {
 };
 
 template <int D, int CT>
-__global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
-  __shared__ __align__(16) DqLds<D> sm;
+__device__ __forceinline__ void bwd_dq_body(const BwdParams& p, DqLds<D>& sm, int bid) {
   constexpr int S = DqLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   const int l32 = lane & 31, hf = lane >> 5;
 
   const int n_rb = p.plan.n_rb, SPL = p.plan.n_split;
-  const int L = xcd_logical_id(blockIdx.x, p.plan.nblk);
+  const int L = xcd_logical_id(bid, p.plan.nblk);
   const int rb = L % n_rb;
   const int split = (L / n_rb) % SPL;
   const int grp = L / (n_rb * SPL);
@@ -126,7 +128,8 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
       for (int e = 0; e < 8; ++e) sdot = fmaf((float)ov[e], (float)oreg[ks][e], sdot);
     }
     dlt = pair_sum(sdot);
-    if (split == 0 && row_ok && hf == 0) p.delta[qrow] = dlt;  // read by bwd_dkdv
+    // read by bwd_dkdv (which, beside this kernel, reads the delta launch's instead)
+    if (split == 0 && row_ok && hf == 0 && !p.plan.dkv_beside) p.delta[qrow] = dlt;
   }
 
   if (tb < te) {
@@ -229,6 +232,12 @@ __global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
   }
 }
 
+template <int D, int CT>
+__global__ __launch_bounds__(NTHR) void bwd_dq_kernel(BwdParams p) {
+  __shared__ __align__(16) DqLds<D> sm;
+  bwd_dq_body<D, CT>(p, sm, (int)blockIdx.x);
+}
+
 // ------------------------------------------------------------------ dK / dV
 constexpr int BQ = 64;                      // packed query rows per step
 constexpr int KB = kDkvKeysPerBlock;        // keys per dK/dV workgroup (128)
@@ -262,9 +271,9 @@ constexpr int NTHR_KV = 512;   // 8 waves: 4 key blocks of 32 x 2 row halves
 // Wave w owns keys kw*32 .. kw*32+31 (kw = w % 4) and row half qb = w / 4 of every
 // step of 64 rows; two waves per SIMD. The keys' K / V rows sit in LDS for the whole
 // launch (the B operands of S and dP); the two row halves' sums meet in LDS at the end.
-template <int D, int CT, bool PREFIX>
-__global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
-  __shared__ __align__(16) DkvLds<D> sm;
+template <int D, int CT, bool PREFIX, bool BESIDE>
+__device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, int bid,
+                                            int nblk) {
   constexpr int S = DkvLds<D>::S;
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
@@ -287,9 +296,19 @@ __global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
   const int RS = p.plan.n_dkv_split;   // > 1: partials for bwd_reduce
   // Neighbouring logical ids (key blocks of one unit) share an XCD and so read the
   // unit's Q / dO rows from that XCD's L2.
-  const int L = xcd_logical_id(blockIdx.x, gridDim.x);
+  // Beside the dQ row blocks, unit j goes to XCD j % 8 as launched: every XCD gets
+  // units of every size, and (with a multiple of 8 (window, KV head) pairs) all units of
+  // one pair share an XCD.
+  const int L = BESIDE ? bid : xcd_logical_id(bid, nblk);
   int rsplit, kblk, grp, RSk;   // RSk: row splits of this key block
-  if (!PREFIX && p.plan.dkv_nkb > 0) {
+  if constexpr (BESIDE) {
+    // beside the dQ row blocks: one unit per key block, largest (block 0) first
+    const int groups = p.B * p.Hkv;
+    kblk = L / groups;
+    grp = L - kblk * groups;
+    rsplit = 0;
+    RSk = 1;
+  } else if (!PREFIX && p.plan.dkv_nkb > 0) {
     const int per = p.plan.dkv_first[nkb];
     grp = L / per;
     const int r = L - grp * per;
@@ -580,6 +599,64 @@ __global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
     }
 }
 
+template <int D, int CT, bool PREFIX>
+__global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
+  __shared__ __align__(16) DkvLds<D> sm;
+  bwd_kv_body<D, CT, PREFIX, false>(p, sm, (int)blockIdx.x, (int)gridDim.x);
+}
+
+// The chunk backward in one grid when the dQ row blocks leave CUs idle: workgroups
+// [0, nblk) are the dQ row blocks, the rest the chunk dK/dV units (one per key block).
+// The hardware starts workgroups in index order, so the units take the idle CUs while
+// the dQ blocks run, and the CUs that free up after.
+template <int D, int CT>
+__global__ __launch_bounds__(NTHR) void bwd_dq_kv_kernel(BwdParams p) {
+  static_assert(NTHR == NTHR_KV, "one block size for both");
+  __shared__ __align__(16) union {
+    DqLds<D> dq;
+    DkvLds<D> kv;
+  } sm;
+  const int bid = (int)blockIdx.x;
+  if (bid < p.plan.nblk)
+    bwd_dq_body<D, CT>(p, sm.dq, bid);
+  else
+    bwd_kv_body<D, kBF16, false, true>(p, sm.kv, bid - p.plan.nblk,
+                                       (int)gridDim.x - p.plan.nblk);
+}
+
+// delta_i = sum_d dO_id * O_id (fp32) of every chunk row, for the dK/dV units that run
+// beside the dQ row blocks: CH = D / 8 consecutive lanes share a row, 8 values each.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+  constexpr int CH = D / 8;
+  const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = idx / CH;
+  const int c8 = (int)(idx % CH);
+  const bool ok = row < nrow;   // every lane takes part in the lane sums below
+  const int64_t r = ok ? row : 0;
+  const u32x4 g = *reinterpret_cast<const u32x4*>(p.d_o + r * D + c8 * 8);
+  const u32x4 o = *reinterpret_cast<const u32x4*>(p.o + r * D + c8 * 8);
+  float dot = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // element copies first: a bit_cast of a subscripted vector element reads element 0
+    const uint32_t gw = g[e], ow = o[e];
+    dot = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, gw),
+                                          __builtin_bit_cast(bf16x2, ow), dot, false);
+  }
+  dot += dpp_f32<0xB1>(dot);    // quad_perm [1, 0, 3, 2]
+  dot += dpp_f32<0x4E>(dot);    // quad_perm [2, 3, 0, 1]
+  dot += dpp_f32<0x141>(dot);   // row_half_mirror: the sum of 8 lanes
+  if constexpr (CH == 16) dot += dpp_f32<0x140>(dot);   // row_mirror: of 16
+  if (ok && c8 == 0) p.delta[row] = dot;
+}
+
 // Sums of split partials, in split order, written as bf16 (one launch for both):
 // threads [0, n_dq) reduce dQ rows (prefix split of the dQ kernel), the rest reduce
 // dK and dV rows (query-row split of the dK/dV kernel).
@@ -644,6 +721,28 @@ template <int D, int CT>
 hipError_t launch_bwd_t(const BwdParams& p, hipStream_t s) {
   const int64_t nrow = (int64_t)p.B * p.Hq * p.C;
   hipError_t e;
+  if (p.plan.dkv_beside) {
+    const int64_t units = (int64_t)p.B * p.Hkv * ((p.C + KB - 1) / KB);
+    prof_begin(PKA_KERNEL_BWD_PREP, s);
+    hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((nrow * (D / 8) + 255) / 256)),
+                       dim3(256), 0, s, p);
+    prof_end(PKA_KERNEL_BWD_PREP, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    prof_begin(PKA_KERNEL_BWD_DQ, s);
+    hipLaunchKernelGGL((bwd_dq_kv_kernel<D, CT>), dim3((unsigned)(p.plan.nblk + units)),
+                       dim3(NTHR), 0, s, p);
+    prof_end(PKA_KERNEL_BWD_DQ, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.plan.n_split > 1) {
+      const int64_t n_dq = nrow * (D / 8);
+      prof_begin(PKA_KERNEL_BWD_DQ_REDUCE, s);
+      hipLaunchKernelGGL((bwd_reduce_kernel<D, false>), dim3((unsigned)((n_dq + 255) / 256)),
+                         dim3(256), 0, s, p, n_dq, (int64_t)0, p.C);
+      prof_end(PKA_KERNEL_BWD_DQ_REDUCE, s);
+      e = hipGetLastError();
+    }
+    return e;
+  }
   prof_begin(PKA_KERNEL_BWD_DQ, s);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CT>), dim3(p.plan.nblk), dim3(NTHR), 0, s, p);
   prof_end(PKA_KERNEL_BWD_DQ, s);

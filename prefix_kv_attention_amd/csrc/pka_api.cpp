@@ -196,6 +196,22 @@ Plan plan_bwd(const pka_dims& d) {
   const int64_t units = groups * nkb;
   pl.n_dkv_split = 1;
   pl.dkv_nkb = 0;
+  pl.dkv_beside = 0;
+  // Beside the dQ row blocks: when every unit (one per key block, all its rows) finds
+  // an idle CU at the start and its steps (64 rows each) are no more than one dQ
+  // workgroup's key tiles (the two cost about the same), the units finish inside the
+  // dQ launch. Units that wait for a CU are not started on the ones the first units
+  // free (measured), so the rule requires one round.
+  if (pl.nblk < kNumCUs) {
+    const int64_t idle = kNumCUs - pl.nblk;
+    const int64_t unit_steps = (G * d.chunk_len + 63) / 64;
+    const int64_t n_tiles = (d.prefix_len + d.chunk_len + kKeysPerTile - 1) / kKeysPerTile;
+    const int64_t dq_tiles = (n_tiles + pl.n_split - 1) / pl.n_split;
+    if (units <= idle && unit_steps <= dq_tiles) {
+      pl.dkv_beside = 1;
+      return pl;
+    }
+  }
   if (units >= kNumCUs) return pl;
   if (nkb <= kMaxDkvTable) {
     int64_t steps[kMaxDkvTable], cnt[kMaxDkvTable];

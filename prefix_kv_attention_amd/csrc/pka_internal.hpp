@@ -41,6 +41,10 @@ struct Plan {
   // of each (window, KV head). dkv_nkb == 0: every block has n_dkv_split splits.
   int dkv_nkb;
   int16_t dkv_first[kMaxDkvTable + 1];
+  // backward only: 1 = the dK/dV units (one per key block, no row split) run in the
+  // same grid as the dQ row blocks, on the CUs those leave idle; delta comes from a
+  // launch before them
+  int dkv_beside;
 };
 
 struct FwdParams {

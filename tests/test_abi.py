@@ -351,6 +351,23 @@ def _dkv_splits(batch, hq, hkv, C, cus=256, kb=128):
     return max(cnt)
 
 
+def _dkv_beside(batch, hq, hkv, P, C, cus=256):
+    """The rule for running the chunk dK/dV units beside the dQ row blocks, restated.
+    dQ grid: one workgroup per 256 packed rows of a (window, KV head); when those are
+    fewer than the CUs, the key tiles are split (each split keeps >= 8 tiles, at most 16
+    splits). Beside: every unit (one per 128-key block) has an idle CU, and a unit's
+    64-row steps (all rows of the group) are no more than one dQ workgroup's key tiles."""
+    G = hq // hkv
+    units = batch * hkv * -(-(G * C) // 256)
+    split = 1
+    if units < cus:
+        split = min(cus // units, max(1, -(-(P + 1) // 64) // 8), 16)
+    nblk = units * split
+    dq_tiles = -(-(-(-(P + C) // 64)) // split)
+    kv_units = batch * hkv * -(-C // 128)
+    return nblk < cus and kv_units <= cus - nblk and -(-(G * C) // 64) <= dq_tiles
+
+
 @pytest.mark.parametrize("shape", [(4, 32, 8, 16384, 512), (2, 12, 2, 16384, 512),
                                    (1, 40, 8, 63488, 512), (1, 4, 1, 1000, 130),
                                    (8, 32, 8, 4096, 512)])
@@ -359,7 +376,13 @@ def test_bwd_workspace_follows_the_dkv_split_rule(pka, shape):
     d = dims(pka, batch=B, n_heads_q=hq, n_heads_kv=hkv, prefix_len=P, chunk_len=C)
     a256 = lambda n: (n + 255) // 256 * 256
     nrow = B * hq * C
-    split = _dkv_splits(B, hq, hkv, C)
+    # dK/dV units beside the dQ blocks are not split
+    beside = _dkv_beside(B, hq, hkv, P, C)
+    split = 1 if beside else _dkv_splits(B, hq, hkv, C)
+    if shape == (2, 12, 2, 16384, 512):
+        assert beside                            # 16 units, 16 idle CUs, 48 <= 53 tiles
+    if shape == (1, 40, 8, 63488, 512):
+        assert not beside                        # 32 units for 16 idle CUs
     want = a256(nrow * 4)
     if split > 1:
         want += a256(split * 2 * B * hkv * C * 128 * 4)
