@@ -608,7 +608,9 @@ __global__ __launch_bounds__(NTHR_KV) void bwd_kv_kernel(BwdParams p) {
 // The chunk backward in one grid when the dQ row blocks leave CUs idle: workgroups
 // [0, nblk) are the dQ row blocks, the rest the chunk dK/dV units (one per key block).
 // The hardware starts workgroups in index order, so the units take the idle CUs while
-// the dQ blocks run, and the CUs that free up after.
+// the dQ blocks run. The plan takes this grid only when every unit has an idle CU from
+// the start and should end within the dQ blocks' time: a unit left waiting was not
+// placed on a CU that an earlier unit freed, only on one a dQ block freed.
 template <int D, int CT>
 __global__ __launch_bounds__(NTHR) void bwd_dq_kv_kernel(BwdParams p) {
   static_assert(NTHR == NTHR_KV, "one block size for both");
