@@ -66,13 +66,40 @@ def prefix_bytes(w):
     return 2 * rows * per_row   # K and V
 
 
+def code_text(src):
+    """C/C++ source with comments removed and whitespace runs collapsed to one space, so
+    that an edit of comments or layout leaves it unchanged (string and character
+    literals are kept as written)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest(files):
-    """First 16 hex digits of the SHA-256 of the kernel sources a figure was taken on."""
+    """First 16 hex digits of the SHA-256 of the code (comments and layout aside) of the
+    kernel sources a figure was taken on."""
     import hashlib
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "prefix_kv_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "prefix_kv_attention_amd", "csrc", f), "r") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -77,3 +77,11 @@ def test_more_than_one_gpu_is_refused_before_any_gpu_work():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_code_text_ignores_comments_and_layout_but_not_code():
+    a = 'int x = 1; // one\n/* two\n   lines */ float y = f("a//b", \'/\');\n'
+    b = 'int x = 1;   // uno\n\nfloat y = f("a//b", \'/\');'
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text(a) != bench.code_text(a.replace("x = 1", "x = 2"))
+    assert '"a//b"' in bench.code_text(a)          # a literal is not a comment
