@@ -245,21 +245,17 @@ constexpr int KB = kDkvKeysPerBlock;        // keys per dK/dV workgroup (128)
 template <int D>
 struct DkvLds {
   static constexpr int S = D + 8;
-  union {
-    struct {
-      uint16_t q[2][BQ * S];
-      uint16_t g[2][BQ * S];   // dO
-      uint16_t k[KB * S];      // the workgroup's keys, row-major (rows permuted by prow)
-      uint16_t v[KB * S];
-    } t;
-    float red[4][32 * D * 2];  // dK^T, dV^T partial sums of the waves of row half 1
-  } u;
+  uint16_t q[2][BQ * S];
+  uint16_t g[2][BQ * S];   // dO
+  // P of the step (fp32), handed from the S / P / dV waves to the dP / dS / dK waves of
+  // the same keys: [key block][row half][group of 4 result registers][lane][4].
+  __align__(16) float pt[4][2][4][64 * 4];
   __align__(16) float lse2[2][BQ];
   __align__(16) float dlt[2][BQ];   // -delta of the staged rows
   __align__(16) int tok[2][BQ];
 };
 
-constexpr int NTHR_KV = 512;   // 8 waves: 4 key blocks of 32 x 2 row halves
+constexpr int NTHR_KV = 512;   // 8 waves: two roles x 4 key blocks of 32
 
 // dK/dV of one block of 128 keys of one (window, KV head), over the packed query
 // rows of all G heads that see them. PREFIX = false: the chunk's own keys (causal:
@@ -268,9 +264,19 @@ constexpr int NTHR_KV = 512;   // 8 waves: 4 key blocks of 32 x 2 row halves
 // chunk row sees them), dequantised on load like the forward; fp32 outputs
 // dkp, dvp [B][Hkv][H][D] whose row h is cache row P_b - H + h (zero when that row
 // does not exist because P_b < H).
-// Wave w owns keys kw*32 .. kw*32+31 (kw = w % 4) and row half qb = w / 4 of every
-// step of 64 rows; two waves per SIMD. The keys' K / V rows sit in LDS for the whole
-// launch (the B operands of S and dP); the two row halves' sums meet in LDS at the end.
+// Waves kw = 0..3 and 4 + kw own keys kw*32 .. kw*32+31 over both 32-row halves of
+// every step of 64 rows, in two roles. Wave kw holds the keys' K rows in registers
+// (the B operand of S = Q K^T), forms P = exp2(S * scale * log2 e - LSE * log2 e) with
+// the causal mask, hands P to LDS in fp32 and adds dV^T += dO^T P. Wave 4 + kw (the
+// other wave of the same SIMD) holds the keys' V rows, forms dP - delta = dO V^T -
+// delta, and after the hand-over dS = P (dP - delta) and dK^T += Q^T dS. So every MFMA
+// reads one operand from LDS, each output element has one owner (no reduction across
+// waves), and the first role's softmax runs while the second role's MFMAs issue. The
+// next step's rows are staged where each role would otherwise wait: the dO rows by the
+// second role after its dP chain, the Q rows by the first role after its dV chain, the
+// LSE / delta by wave 0 after its softmax. Two barriers per step: P is written, and the
+// step's tiles are free again. The S and dP chains read all their LDS operands before
+// the first MFMA (read two ahead, each pair of MFMAs waited for a read).
 template <int D, int CT, bool PREFIX, bool BESIDE>
 __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, int bid,
                                             int nblk) {
@@ -278,16 +284,17 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, i
   constexpr int NKS = D / 16;
   constexpr int NDB = D / 32;
   constexpr int CH = D / 8;
-  constexpr int RT = 2 * BQ * CH / NTHR_KV;   // rows a thread stages per step (4 or 2)
-  constexpr int NT = (BQ / RT) * CH;          // staging tasks per tensor (one per thread)
+  constexpr int NRT = NTHR_KV / 2;            // threads of one role
+  constexpr int RT = BQ * CH / NRT;           // rows a thread stages per step (4 or 2)
   static_assert(KB == 32 * 4, "four key blocks of 32");
-  static_assert(2 * NT == NTHR_KV, "one staging task per thread");
+  static_assert(RT * NRT == BQ * CH, "one staging task per thread of a role");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hf = lane >> 5;
-  const int kw = wave & 3;       // key block of this wave
-  const int qb = wave >> 2;      // row half of every step this wave takes
+  const int kw = wave & 3;           // key block of this wave
+  const bool second = wave >= 4;     // dP / dS / dK role
   const int C = (int)p.C;
   const int G = p.G;
   const int rows = G * C;
@@ -329,42 +336,33 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, i
   // A prefix row that does not exist (P_b < H) contributes and gets exactly zero.
   const bool key_ok = key < NK && (!PREFIX || Pb - NK + key >= 0);
 
-  // The workgroup's 128 K and V rows into LDS (8 rows-of-8 per thread), converted to
-  // bf16; missing keys are zero rows.
+  // This wave's fixed MFMA operand: the K (first role) or V (second role) row of key
+  // `key`, converted to bf16, as the B operand of S or dP: k-step ks of lane (l32, hf)
+  // is values ks*16 + hf*8 .. +7. Missing keys are zero rows.
+  bf16x8 kvop[NKS];
   {
     constexpr int ESZ = (CT == kQ8) ? 1 : 2;
-    const char* ck = static_cast<const char*>(p.cache.k) + bh * p.cache.cap * D * ESZ;
-    const char* cv = static_cast<const char*>(p.cache.v) + bh * p.cache.cap * D * ESZ;
-    const uint16_t* cks = (CT == kQ8) ? p.cache.ks + bh * p.cache.cap * (D / 32) : nullptr;
-    const uint16_t* cvs = (CT == kQ8) ? p.cache.vs + bh * p.cache.cap * (D / 32) : nullptr;
+    const char* base = static_cast<const char*>(second ? p.cache.v : p.cache.k) +
+                       bh * p.cache.cap * D * ESZ;
+    const uint16_t* scl =
+        (CT == kQ8) ? (second ? p.cache.vs : p.cache.ks) + bh * p.cache.cap * (D / 32) : nullptr;
+    const uint16_t* crow = (second ? p.vc : p.kc) + (bh * C + key) * D;
+    const int64_t j = Pb - NK + key;   // cache row of a prefix key
 #pragma unroll
-    for (int it = 0; it < (2 * KB * CH) / NTHR_KV; ++it) {
-      const int task = it * NTHR_KV + tid;
-      const bool is_v = task >= KB * CH;
-      const int tk = is_v ? task - KB * CH : task;
-      const int kr = tk / CH, d0 = (tk % CH) * 8;
-      const int kk = kblk * KB + kr;       // key index of the row
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int d0 = ks * 16 + hf * 8;
       u32x4 w = u32x4{0u, 0u, 0u, 0u};
       if constexpr (PREFIX) {
-        const int64_t j = Pb - NK + kk;    // cache row
-        if (kk < NK && j >= 0) {
+        if (key_ok) {
           RawRow8 r;
-          load_row8<CT, D>(r, is_v ? cv : ck, is_v ? cvs : cks, nullptr, Pb, 0, j, d0);
+          load_row8<CT, D>(r, base, scl, nullptr, Pb, 0, j, d0);
           w = to_bf16x8<CT>(r, true);
         }
       } else {
-        if (kk < NK)
-          w = *reinterpret_cast<const u32x4*>((is_v ? p.vc : p.kc) + (bh * C + kk) * D + d0);
+        if (key < NK) w = *reinterpret_cast<const u32x4*>(crow + d0);
       }
-      *reinterpret_cast<u32x4*>(&(is_v ? sm.u.t.v : sm.u.t.k)[prow(kr) * S + d0]) = w;
+      kvop[ks] = __builtin_bit_cast(bf16x8, w);
     }
-  }
-
-  f32x16 acck[NDB], accv[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-    acck[db] = f32x16{};
-    accv[db] = f32x16{};
   }
   const float c = p.scale_log2;
 
@@ -375,63 +373,48 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, i
   const int s_hi = (int)((int64_t)(rsplit + 1) * steps_unit / RSk);
   const int r_begin = r_unit + s_lo * BQ;   // this split's rows
   const int n_steps = s_hi - s_lo;
-  const bool is_g = tid >= NT;             // stages dO rows (else Q rows)
-  const int ts = is_g ? tid - NT : tid;
-  const int tr0 = (ts / CH) * RT, td0 = (ts % CH) * 8;
-  const uint16_t* src_base = is_g ? p.d_o : p.q;
-
-  // Packed row rr is token rr / G of query head kv*G + rr % G. Each thread follows
-  // its rows from step to step (+BQ rows per step) without dividing.
+  // Packed rows from clean_from on have tokens >= the block's last key: no mask.
+  const int clean_from = (kblk * KB + KB - 1) * G;
+  // Packed row rr is token rr / G of query head kv*G + rr % G, at row offset
+  // (rr % G) * C + rr / G from the first row of that head. Each thread follows its rows
+  // from step to step (+BQ packed rows) without dividing.
   const int dt_step = BQ / G, dg_step = BQ % G;
   const int64_t head0 = (int64_t)b * p.Hq + kv * G;   // first query head of this KV head
-  int tq[RT], gq[RT];     // (token, head-in-group) of the staged rows
-  int tl = 0, gl = 0;     // same for the row whose LSE / delta this thread stages
-  {
-#pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int rr = r_begin + tr0 + i;
-      tq[i] = rr / G;
-      gq[i] = rr - tq[i] * G;
-    }
-    const int rr = r_begin + tid;
-    tl = rr / G;
-    gl = rr - tl * G;
-  }
-  auto advance = [&](int& t, int& g) {
-    t += dt_step;
+  const int ro_step = dg_step * C + dt_step;           // row offset change per step
+  const int ro_wrap = 1 - G * C;                       // ... plus this when g wraps
+  auto advance = [&](int& ro, int& g) {
+    ro += ro_step;
     g += dg_step;
     if (g >= G) {
       g -= G;
-      t += 1;
+      ro += ro_wrap;
     }
   };
+  auto start = [&](int rr, int& ro, int& g) {
+    const int t = rr / G;
+    g = rr - t * G;
+    ro = g * C + t;
+  };
+  // Row staging: the first role moves the Q rows of a step, the second the dO rows,
+  // each thread RT rows of 8 values, loaded a step ahead of the LDS write.
+  const int ts = tid & (NRT - 1);
+  const int tr0 = (ts / CH) * RT, td0 = (ts % CH) * 8;
+  const uint16_t* src_head = (second ? p.d_o : p.q) + head0 * C * D + td0;
+  uint16_t* const dst0 = second ? sm.g[0] : sm.q[0];
+  int ro[RT], gq[RT];   // row offset from the head's first row, head in the group
+#pragma unroll
+  for (int i = 0; i < RT; ++i) start(r_begin + tr0 + i, ro[i], gq[i]);
   u32x4 rq[RT];
-  float pl = 0.f, pd = 0.f;   // raw LSE and delta of the staged row: they are scaled
-  int ptok = -1;              // when written to LDS, a step after their loads
-  int rows_left = 0;          // rows of the issued step that exist (>= BQ: all)
+  int rows_left = 0;   // rows of the issued step that exist (>= BQ: all)
   auto issue = [&](int step) {   // called for steps 0, 1, 2, ... in order
-    const int r0 = r_begin + step * BQ;
-    // LSE / delta first: the loads complete in order, so a wait that the compiler
-    // may place for them does not also wait for the row loads below.
-    if (tid < BQ) {
-      // Unconditional loads (a padding row reads token 0 of the first head): any
-      // use of a loaded value here would wait for every load in flight.
-      const bool valid = r0 + tid < rows;
-      const int64_t row = valid ? (head0 + gl) * C + tl : head0 * C;
-      pl = p.lse[row];
-      pd = p.delta[row];
-      ptok = valid ? tl : -1;
-      advance(tl, gl);
-    }
-    // Rows past the last one (only in the last step) load a valid row and are zeroed
-    // when staged: no register is written here but by the loads themselves.
-    rows_left = rows - r0;
+    // Rows past the last one (only in the last step) load the head's first row and
+    // are zeroed when staged: no register is written here but by the loads themselves.
+    rows_left = rows - (r_begin + step * BQ);
 #pragma unroll
     for (int i = 0; i < RT; ++i) {
-      const bool ok = tr0 + i < rows_left;
-      const int64_t row = ok ? (head0 + gq[i]) * C + tq[i] : head0 * C;
-      rq[i] = *reinterpret_cast<const u32x4*>(src_base + row * D + td0);
-      advance(tq[i], gq[i]);
+      const int off = tr0 + i < rows_left ? ro[i] : 0;
+      rq[i] = *reinterpret_cast<const u32x4*>(src_head + (int64_t)off * D);
+      advance(ro[i], gq[i]);
     }
   };
   auto stage = [&](int buf) {
@@ -440,162 +423,272 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, i
       for (int i = 0; i < RT; ++i)
         if (tr0 + i >= rows_left) rq[i] = u32x4{0u, 0u, 0u, 0u};
     }
-    uint16_t* dst = is_g ? sm.u.t.g[buf] : sm.u.t.q[buf];
+    uint16_t* dst = dst0 + buf * (BQ * S);
 #pragma unroll
     for (int i = 0; i < RT; ++i)
       *reinterpret_cast<u32x4*>(&dst[prow(tr0 + i) * S + td0]) = rq[i];
-    if (tid < BQ) {
-      const bool valid = ptok >= 0;
-      sm.lse2[buf][tid] = valid ? pl * kLog2e : 0.f;
-      sm.dlt[buf][tid] = valid ? -pd : 0.f;   // negated: the dP chain starts from it
-      sm.tok[buf][tid] = ptok;
-    }
   };
-
-  const int a_off = (qb * 32 + prow(l32)) * S + hf * 8;   // this wave's rows of a step
-  const int k_off = (kw * 32 + prow(l32)) * S + hf * 8;   // this wave's keys
-  const TrOffsets t_off = tr_lane_offsets<S>(lane);
-
   if (n_steps > 0) {
     issue(0);
     stage(0);
     if (n_steps > 1) issue(1);
   }
-  __syncthreads();   // the K / V rows and step 0's rows are in LDS
-  // One wait for every load so far (step 1's rows): otherwise the compiler waits at
-  // the loop top on each iteration, and that wait also covers the rows just requested
-  // for two steps ahead.
-  wait_global_loads();
-  // Packed rows from clean_from on have tokens >= the block's last key: no mask.
-  const int clean_from = (kblk * KB + KB - 1) * G;
-  for (int step = 0; step < n_steps; ++step) {
-    const int cur = step & 1;
-    const uint16_t* qt = sm.u.t.q[cur];
-    const uint16_t* gt = sm.u.t.g[cur];
-    const bool diag = !PREFIX && r_begin + step * BQ < clean_from;
-    // S and dP (rows x keys) of this wave's 32 rows and 32 keys; dP starts from
-    // -delta of its rows, so the chain yields dP - delta. Register i of a result is
-    // row (i / 4) * 8 + hf * 4 + i % 4 of the half, key l32.
-    f32x16 sv = f32x16{}, dp;
-#pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][qb * 32 + g4 * 8 + hf * 4]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) dp[g4 * 4 + j] = d4[j];
+
+  float* ptw = &sm.pt[kw][0][0][lane * 4];   // this key block's P, lane's 4 values
+  const int a_off = prow(l32) * S + hf * 8;  // operand rows of row half 0 of a step
+  const TrOffsets t_off = tr_lane_offsets<S>(lane);
+
+  if (!second) {
+    // Wave 0 stages the LSE, -delta and token of every row of a step (one row per
+    // lane), loads a step ahead of the LDS write.
+    const float* lse_head = p.lse + head0 * C;
+    const float* dlt_head = p.delta + head0 * C;
+    int rol = 0, gl = 0;
+    start(r_begin + lane, rol, gl);
+    float pl = 0.f, pd = 0.f;   // raw LSE and delta: scaled when written to LDS
+    int ptok = -1;
+    auto issue_l = [&](int step) {
+      // Unconditional loads (a padding row reads the first row of the head): any use
+      // of a loaded value here would wait for the load.
+      const bool valid = r_begin + step * BQ + lane < rows;
+      const int off = valid ? rol : 0;
+      pl = lse_head[off];
+      pd = dlt_head[off];
+      ptok = valid ? (rol - gl * C) : -1;
+      advance(rol, gl);
+    };
+    auto stage_l = [&](int buf) {
+      const bool valid = ptok >= 0;
+      sm.lse2[buf][lane] = valid ? pl * kLog2e : 0.f;
+      sm.dlt[buf][lane] = valid ? -pd : 0.f;   // negated: the dP chain starts from it
+      sm.tok[buf][lane] = ptok;
+    };
+    if (wave == 0 && n_steps > 0) {
+      issue_l(0);
+      stage_l(0);
+      if (n_steps > 1) issue_l(1);
     }
+    f32x16 accv[NDB];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      sv = mfma32(*reinterpret_cast<const bf16x8*>(&qt[a_off + ks * 16]),
-                  *reinterpret_cast<const bf16x8*>(&sm.u.t.k[k_off + ks * 16]), sv);
-      dp = mfma32(*reinterpret_cast<const bf16x8*>(&gt[a_off + ks * 16]),
-                  *reinterpret_cast<const bf16x8*>(&sm.u.t.v[k_off + ks * 16]), dp);
-    }
-    bf16x8 pb[2], dsb[2];
+    for (int db = 0; db < NDB; ++db) accv[db] = f32x16{};
+    __syncthreads();   // step 0's rows are in LDS
+    // One wait for the fixed operand (and wave 0's first LSE / delta loads): otherwise
+    // the compiler waits for every load at the loop top, the next steps' ones included.
+    wait_global_loads();
+    for (int step = 0; step < n_steps; ++step) {
+      const int cur = step & 1;
+      const uint16_t* qt = sm.q[cur];
+      const uint16_t* gt = sm.g[cur];
+      const bool diag = !PREFIX && r_begin + step * BQ < clean_from;
+      // S of this wave's 32 keys over both row halves. Register i of a result is row
+      // (i / 4) * 8 + hf * 4 + i % 4 of the half, key l32.
+      f32x16 sv[2] = {f32x16{}, f32x16{}};
+      bf16x8 opa[2][NKS];
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      // result rows (g4*8 + hf*4 + 0..3) of the half: one 16-byte read per array
-      const int q0 = qb * 32 + g4 * 8 + hf * 4;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
-      const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
-      const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
+      for (int rh = 0; rh < 2; ++rh)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = g4 * 4 + j;
-        const float e = __builtin_amdgcn_exp2f(fmaf(sv[i], c, -l4[j]));
-        // Prefix keys are seen by every row; padding rows past the last one have
-        // zero q and dO and so add nothing. Chunk keys: causal, checked only in
-        // the steps that reach below the block's last key.
-        const float pv = (!PREFIX && diag && key > tk[j]) ? 0.f : e;
-        pb[i >> 3][i & 7] = (__bf16)pv;
-        dsb[i >> 3][i & 7] = (__bf16)(pv * dp[i]);
+        for (int ks = 0; ks < NKS; ++ks)
+          opa[rh][ks] = *reinterpret_cast<const bf16x8*>(&qt[a_off + rh * 32 * S + ks * 16]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sv[rh] = mfma32(opa[rh][ks], kvop[ks], sv[rh]);
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q0 = rh * 32 + g4 * 8 + hf * 4;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sm.lse2[cur][q0]);
+          const int4 t4 = *reinterpret_cast<const int4*>(&sm.tok[cur][q0]);
+          const int tk[4] = {t4.x, t4.y, t4.z, t4.w};
+          f32x4 pf;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int i = g4 * 4 + jj;
+            const float e = __builtin_amdgcn_exp2f(fmaf(sv[rh][i], c, -l4[jj]));
+            // Prefix keys are seen by every row; padding rows past the last one have
+            // zero q and dO and so add nothing. Chunk keys: causal, checked only in
+            // the steps that reach below the block's last key.
+            const float pv = (!PREFIX && diag && key > tk[jj]) ? 0.f : e;
+            pf[jj] = pv;
+            pb[rh][i >> 3][i & 7] = (__bf16)pv;
+          }
+          *reinterpret_cast<f32x4*>(ptw + (rh * 4 + g4) * 256) = pf;
+        }
+      // The next step's LSE / delta go to the other buffer, read last in the previous step.
+      if (wave == 0 && step + 1 < n_steps) {
+        stage_l(cur ^ 1);
+        if (step + 2 < n_steps) issue_l(step + 2);
       }
+      __syncthreads();   // P is in LDS
+#pragma unroll
+      for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss)
+            accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, rh * 32 + ss * 16, db * 32),
+                              pb[rh][ss], accv[db]);
+      // The next step's Q rows go to the other buffer, read last in the previous step.
+      if (step + 1 < n_steps) {
+        stage(cur ^ 1);
+        if (step + 2 < n_steps) issue(step + 2);
+      }
+      __syncthreads();   // this step's tiles and P are free
     }
+    if (key >= NK) return;
+    if (PREFIX && RS == 1) {
+      float* pv = p.dvp + (bh * NK + key) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hf * 4;
+          *reinterpret_cast<f32x4*>(pv + d) =
+              key_ok ? f32x4{accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1], accv[db][g4 * 4 + 2],
+                             accv[db][g4 * 4 + 3]}
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      return;
+    }
+    if (RS > 1) {
+      // fp32 partials of this row split, summed in split order by bwd_reduce.
+      const int64_t nkey = (int64_t)p.B * p.Hkv * NK;
+      float* pv = p.ws_dkv + ((int64_t)rsplit * 2 * nkey + nkey + bh * NK + key) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + g4 * 8 + hf * 4;
+          *reinterpret_cast<f32x4*>(pv + d) =
+              key_ok ? f32x4{accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1], accv[db][g4 * 4 + 2],
+                             accv[db][g4 * 4 + 3]}
+                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      return;
+    }
+    uint16_t* dvp = p.dv + (bh * C + key) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        accv[db] = mfma32(lds_tr_operand<S>(gt, t_off, qb * 32 + ss * 16, db * 32), pb[ss], accv[db]);
-        acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, qb * 32 + ss * 16, db * 32), dsb[ss], acck[db]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = db * 32 + g4 * 8 + hf * 4;
+        u32x2 wv;
+        wv.x = pack_bf16(accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1]);
+        wv.y = pack_bf16(accv[db][g4 * 4 + 2], accv[db][g4 * 4 + 3]);
+        *reinterpret_cast<u32x2*>(dvp + d) = wv;
       }
+    return;
+  }
+
+  // ---- second role: dP, dS, dK
+  f32x16 acck[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acck[db] = f32x16{};
+  __syncthreads();   // step 0's rows are in LDS
+  // One wait for every load so far (the fixed operand, step 1's rows): otherwise the
+  // compiler waits at the loop top on each iteration, and that wait also covers the
+  // rows just requested for two steps ahead.
+  wait_global_loads();
+  for (int step = 0; step < n_steps; ++step) {
+    const int cur = step & 1;
+    const uint16_t* qt = sm.q[cur];
+    const uint16_t* gt = sm.g[cur];
+    // dP of this wave's keys over both row halves; the chain starts from -delta of
+    // its rows, so it yields dP - delta (register layout as S).
+    f32x16 dp[2];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sm.dlt[cur][rh * 32 + g4 * 8 + hf * 4]);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) dp[rh][g4 * 4 + jj] = d4[jj];
+      }
+    bf16x8 opa[2][NKS];
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        opa[rh][ks] = *reinterpret_cast<const bf16x8*>(&gt[a_off + rh * 32 * S + ks * 16]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        dp[rh] = mfma32(opa[rh][ks], kvop[ks], dp[rh]);
+    // The next step's dO rows go to the other buffer, read last in the previous step.
     if (step + 1 < n_steps) {
       stage(cur ^ 1);
       if (step + 2 < n_steps) issue(step + 2);
     }
-    __syncthreads();
-  }
-
-  // The waves of row half 1 hand their sums to those of half 0 through LDS (fp32, a
-  // fixed order); the LDS tiles are no longer read after the loop's last barrier.
-  float* red = sm.u.red[kw];
-  if (qb == 1) {
+    __syncthreads();   // P is in LDS
+    bf16x8 dsb[2][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+    for (int rh = 0; rh < 2; ++rh)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        red[(db * 16 + i) * 64 + lane] = acck[db][i];
-        red[32 * D + (db * 16 + i) * 64 + lane] = accv[db][i];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 pf = *reinterpret_cast<const f32x4*>(ptw + (rh * 4 + g4) * 256);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = g4 * 4 + jj;
+          dsb[rh][i >> 3][i & 7] = (__bf16)(pf[jj] * dp[rh][i]);
+        }
       }
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss)
+          acck[db] = mfma32(lds_tr_operand<S>(qt, t_off, rh * 32 + ss * 16, db * 32),
+                            dsb[rh][ss], acck[db]);
+    __syncthreads();   // this step's tiles and P are free
   }
-  __syncthreads();
-  if (qb == 1 || key >= NK) return;
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      acck[db][i] = key_ok ? acck[db][i] + red[(db * 16 + i) * 64 + lane] : 0.f;
-      accv[db][i] = key_ok ? accv[db][i] + red[32 * D + (db * 16 + i) * 64 + lane] : 0.f;
-    }
+  if (key >= NK) return;
   const float sc = p.scale;
   if (PREFIX && RS == 1) {
     float* pk = p.dkp + (bh * NK + key) * D;
-    float* pv = p.dvp + (bh * NK + key) * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hf * 4;
         *reinterpret_cast<f32x4*>(pk + d) =
-            f32x4{acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc,
-                  acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc};
-        *reinterpret_cast<f32x4*>(pv + d) =
-            f32x4{accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1], accv[db][g4 * 4 + 2],
-                  accv[db][g4 * 4 + 3]};
+            key_ok ? f32x4{acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc,
+                           acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc}
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     return;
   }
   if (RS > 1) {
-    // fp32 partials of this row split, summed in split order by bwd_reduce.
     const int64_t nkey = (int64_t)p.B * p.Hkv * NK;
     float* pk = p.ws_dkv + ((int64_t)rsplit * 2 * nkey + bh * NK + key) * D;
-    float* pv = pk + nkey * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = db * 32 + g4 * 8 + hf * 4;
         *reinterpret_cast<f32x4*>(pk + d) =
-            f32x4{acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc,
-                  acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc};
-        *reinterpret_cast<f32x4*>(pv + d) =
-            f32x4{accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1], accv[db][g4 * 4 + 2],
-                  accv[db][g4 * 4 + 3]};
+            key_ok ? f32x4{acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc,
+                           acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc}
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     return;
   }
   uint16_t* dkp = p.dk + (bh * C + key) * D;
-  uint16_t* dvp = p.dv + (bh * C + key) * D;
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = db * 32 + g4 * 8 + hf * 4;
-      u32x2 wk, wv;
+      u32x2 wk;
       wk.x = pack_bf16(acck[db][g4 * 4 + 0] * sc, acck[db][g4 * 4 + 1] * sc);
       wk.y = pack_bf16(acck[db][g4 * 4 + 2] * sc, acck[db][g4 * 4 + 3] * sc);
-      wv.x = pack_bf16(accv[db][g4 * 4 + 0], accv[db][g4 * 4 + 1]);
-      wv.y = pack_bf16(accv[db][g4 * 4 + 2], accv[db][g4 * 4 + 3]);
       *reinterpret_cast<u32x2*>(dkp + d) = wk;
-      *reinterpret_cast<u32x2*>(dvp + d) = wv;
     }
 }
 
