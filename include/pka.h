@@ -41,7 +41,10 @@
  *  - Calls that overlap on one stream are ordered; calls on different streams that
  *    share output buffers race (the caller orders them).
  *  - Limits: D in {64, 128}; 1 <= C <= 65536; 0 <= P; P + C <= 2^31 - 1;
- *    B * Hq * C <= 2^31 - 1.
+ *    B * Hq * C <= 2^31 - 1. The backward calls (pka_chunk_attn_bwd,
+ *    pka_chunk_attn_bwd_noalloc, pka_prefix_kv_grad) also need the query rows of one
+ *    KV head below 4 GiB: (Hq / Hkv) * C * D * 2 <= 2^32 - 2^20 bytes, else
+ *    PKA_ERR_DIMS.
  */
 #ifndef PKA_H
 #define PKA_H

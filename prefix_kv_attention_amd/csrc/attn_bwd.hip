@@ -396,25 +396,45 @@ __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, i
     ro = g * C + t;
   };
   // Row staging: the first role moves the Q rows of a step, the second the dO rows,
-  // each thread RT rows of 8 values, loaded a step ahead of the LDS write.
+  // each thread RT rows of 8 values, loaded a step ahead of the LDS write. The rows of
+  // the G query heads of this KV head are one block of G * C rows (under 4 GiB, checked
+  // by the host); buffer loads address it with 32-bit byte offsets, and an offset past
+  // its end (a padding row of the last step) reads zero instead of faulting.
   const int ts = tid & (NRT - 1);
   const int tr0 = (ts / CH) * RT, td0 = (ts % CH) * 8;
-  const uint16_t* src_head = (second ? p.d_o : p.q) + head0 * C * D + td0;
+  const __amdgpu_buffer_rsrc_t rows_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>((second ? p.d_o : p.q) + head0 * C * D), 0,
+      (int)((uint32_t)G * (uint32_t)C * (uint32_t)(D * 2)), 0x00020000);
   uint16_t* const dst0 = second ? sm.g[0] : sm.q[0];
-  int ro[RT], gq[RT];   // row offset from the head's first row, head in the group
+  uint32_t rb[RT];   // byte offset of each staged row's 8 values in the block
+  int gq[RT];        // head in the group of each staged row
 #pragma unroll
-  for (int i = 0; i < RT; ++i) start(r_begin + tr0 + i, ro[i], gq[i]);
+  for (int i = 0; i < RT; ++i) {
+    int ro;
+    start(r_begin + tr0 + i, ro, gq[i]);
+    rb[i] = (uint32_t)ro * (D * 2) + td0 * 2;
+  }
+  const uint32_t rb_step = (uint32_t)ro_step * (D * 2);
+  const uint32_t rb_wrap = (uint32_t)ro_wrap * (D * 2);   // modulo 2^32
   u32x4 rq[RT];
   int rows_left = 0;   // rows of the issued step that exist (>= BQ: all)
   auto issue = [&](int step) {   // called for steps 0, 1, 2, ... in order
-    // Rows past the last one (only in the last step) load the head's first row and
-    // are zeroed when staged: no register is written here but by the loads themselves.
     rows_left = rows - (r_begin + step * BQ);
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-      const int off = tr0 + i < rows_left ? ro[i] : 0;
-      rq[i] = *reinterpret_cast<const u32x4*>(src_head + (int64_t)off * D);
-      advance(ro[i], gq[i]);
+    for (int i = 0; i < RT; ++i)
+      rq[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rows_rsrc, (int)rb[i], 0, 0));
+    if (dg_step == 0) {   // G divides BQ: every row moves BQ / G tokens
+#pragma unroll
+      for (int i = 0; i < RT; ++i) rb[i] += rb_step;
+    } else {
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        gq[i] += dg_step;
+        const bool wrap = gq[i] >= G;
+        gq[i] -= wrap ? G : 0;
+        rb[i] += rb_step + (wrap ? rb_wrap : 0u);
+      }
     }
   };
   auto stage = [&](int buf) {

@@ -35,6 +35,8 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 constexpr int64_t kMaxChunk = 65536;
 constexpr int64_t kMaxSeq = 2147483647LL;
+// Q / dO rows of one KV head in the backward, with room for one step of padding rows.
+constexpr int64_t kMaxGroupRowBytes = (1LL << 32) - (1LL << 20);
 
 pka_status check_dims(const pka_dims* d) {
   if (!d) return fail(PKA_ERR_NULL, "dims is NULL");
@@ -58,6 +60,18 @@ pka_status check_dims(const pka_dims* d) {
     return fail(PKA_ERR_DIMS, "softmax_scale must be finite and > 0");
   if ((reinterpret_cast<uintptr_t>(d->prefix_lens) & 3u) != 0)
     return fail(PKA_ERR_ALIGN, "prefix_lens not 4-byte aligned");
+  return PKA_OK;
+}
+
+// The backward kernels address the Q / dO rows of one KV head's query heads (G * C rows
+// of D bf16 values) with 32-bit byte offsets.
+pka_status check_group_rows(const pka_dims* d) {
+  const int64_t bytes =
+      (int64_t)(d->n_heads_q / d->n_heads_kv) * d->chunk_len * d->head_dim * 2;
+  if (bytes > kMaxGroupRowBytes)
+    return fail(PKA_ERR_DIMS,
+                "the query rows of one KV head (group * chunk_len * head_dim * 2 bytes) "
+                "must stay below 4 GiB");
   return PKA_OK;
 }
 
@@ -390,6 +404,7 @@ pka_status pka_chunk_attn_bwd(const pka_dims* dims, const void* q, const void* k
   g_last_error[0] = 0;
   pka_status st;
   if ((st = check_dims(dims)) != PKA_OK) return st;
+  if ((st = check_group_rows(dims)) != PKA_OK) return st;
   if ((st = check_ptrs({q, k, v, o, lse, d_o, dq, dk, dv}, "q, k, v, o, lse, d_o, dq, dk, dv")) !=
       PKA_OK)
     return st;
@@ -512,6 +527,7 @@ pka_status pka_prefix_kv_grad(const pka_dims* dims, int64_t horizon, const void*
   g_last_error[0] = 0;
   pka_status st;
   if ((st = check_dims(dims)) != PKA_OK) return st;
+  if ((st = check_group_rows(dims)) != PKA_OK) return st;
   if ((st = check_horizon(dims, horizon)) != PKA_OK) return st;
   if ((st = check_ptrs({q, lse, d_o, delta, dk_prefix, dv_prefix},
                        "q, lse, d_o, delta, dk_prefix, dv_prefix")) != PKA_OK)

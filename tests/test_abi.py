@@ -146,6 +146,17 @@ def test_bwd_validation(pka):
     assert bwd(pka, dims(pka, n_heads_kv=3), cache(pka))[0] == 2
 
 
+def test_backward_rejects_query_rows_of_one_kv_head_over_4gib(pka):
+    # 256 query heads per KV head x 65536 rows x 128 values x 2 bytes = 4 GiB: the
+    # backward kernels address one KV head's Q / dO rows with 32-bit byte offsets.
+    d = dims(pka, n_heads_q=256, n_heads_kv=1, chunk_len=65536)
+    st, msg = bwd(pka, d, cache(pka))
+    assert st == 2 and "4 GiB" in msg, (st, msg)
+    st = pka.lib.pka_prefix_kv_grad(ctypes.byref(d), 64, A, ctypes.byref(cache(pka)), A, A, A,
+                                    A, A, A, 1 << 40, None)
+    assert st == 2 and "4 GiB" in pka.lib.pka_last_error().decode()
+
+
 def test_append_validation(pka):
     lib = pka.lib
     d = dims(pka, prefix_len=500, chunk_len=64)
