@@ -25,11 +25,11 @@
 //                query rows of all G heads that can see them (token >= key) in tiles
 //                of 64: S = Q K^T and dP = dO V^T with keys as MFMA columns, then
 //                dV^T += dO^T P and dK^T += Q^T dS (dO^T, Q^T by transposing reads).
-//                8 waves, two per SIMD: wave w owns 32 keys (w % 4) and one 32-row
-//                half (w / 4) of every tile; the 128 keys' K / V rows stay in LDS
-//                as MFMA operands, and a staged tile serves all 128 keys (half the
-//                query-row re-reads of 64-key blocks). The two halves' sums meet in
-//                LDS at the end.
+//                8 waves, two per SIMD, in two roles over the same 32 keys: one wave
+//                holds their K rows in registers and forms S, P and dV, the other
+//                holds their V rows and forms dP, dS and dK, taking P from LDS. A
+//                staged tile serves all 128 keys (half the query-row re-reads of
+//                64-key blocks).
 //                The sum over the G heads of a KV head falls out of the packing.
 //                When (window, KV head, key block) units are few, each is split
 //                over disjoint query-row ranges (a key block gets splits in
