@@ -276,7 +276,8 @@ constexpr int NTHR_KV = 512;   // 8 waves: two roles x 4 key blocks of 32
 // second role after its dP chain, the Q rows by the first role after its dV chain, the
 // LSE / delta by wave 0 after its softmax. Two barriers per step: P is written, and the
 // step's tiles are free again. The S and dP chains read all their LDS operands before
-// the first MFMA (read two ahead, each pair of MFMAs waited for a read).
+// their first MFMA (left to the compiler, the reads ran two MFMAs ahead and each pair of
+// MFMAs waited out one read).
 template <int D, int CT, bool PREFIX, bool BESIDE>
 __device__ __forceinline__ void bwd_kv_body(const BwdParams& p, DkvLds<D>& sm, int bid,
                                             int nblk) {
