@@ -21,8 +21,9 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller. The library
- *    allocates nothing and keeps no state between calls (except the opt-in
- *    profiling counters at the end of this file).
+ *    allocates nothing and keeps no state between calls, except the opt-in
+ *    profiling counters at the end of this file and the fixed per-GPU device array
+ *    that pka_chunk_attn_bwd_noalloc uses as its workspace.
  *  - Layouts are dense row-major with the innermost dimension contiguous:
  *      q, o, dO, dq        bf16 [B][Hq][C][D]
  *      k, v, dk, dv        bf16 [B][Hkv][C][D]     (the chunk's own keys/values)
